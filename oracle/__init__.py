@@ -1,0 +1,14 @@
+"""CPU oracle for the SAW-INT4 KV-cache path (numpy, float32 IEEE).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the package smoke check and
+the benchmark's CPU-baseline leg, never by the product path. It shares no code
+with the HIP library and imports nothing from it.
+
+Parity pins (what fixes each function other than itself) are listed in
+tests/test_oracle_pins.py; every function here is pinned.
+"""
+from .sawint4 import (  # noqa: F401
+    F16_MAX, ROT_K, ROT_KV, ROT_NONE, c_h, decode_vectors, dequant_gather,
+    encode_vectors, fwht_blocks, mse, pack_nibbles, quantize,
+    quantize_append, quantize_with_scale, rotate, token_scale, unpack_nibbles,
+)
