@@ -1,0 +1,156 @@
+/*
+ * sawkv — fused block-diagonal Hadamard rotation + token-wise INT4 append into
+ * a paged KV cache, and the matching dequantise / inverse-rotate read-back,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources: youngju.dev reading of the SAW-INT4 preprint,
+ * sections "Why Naive INT4 Breaks", "The Rotation Trick - Block-Diagonal
+ * Hadamard" and the fused-kernel diagram in "The System Is the Design - A
+ * Fused Kernel"; gist.science summary "SAW-INT4: System-Aware 4-Bit KV-Cache
+ * Quantization for Real-World LLM Serving", §2 Metodologia, BDR items 1-3,
+ * and §4 Risultati Sperimentali for h = 128 and keys-only rotation):
+ *
+ *   for every new token t and head j, for K and (unless skipped) V:
+ *     x  = the fp16 head vector, widened to float32 (exact)
+ *     y  = f32(c_h * F_h(x))   when the tensor is rotated, else y = x
+ *          F_h: Sylvester Walsh-Hadamard butterflies inside each block of h
+ *          contiguous channels, strides 1, 2, ..., h/2 in that order, each
+ *          (a, b) -> (a + b, a - b) rounded to float32; c_h = f32(1/sqrt(h))
+ *     s  = f16(f32(max_i |y_i| / 7)), saturated to 65504
+ *     q_i = clamp(rint_half_even(f32(y_i / s)), -8, 7); s == 0 -> q = 0
+ *     codes[slot][j][k] = (q_{2k} & 15) | (q_{2k+1} & 15) << 4
+ *     scales[slot][j]   = s
+ *   where slot = slot_mapping[t] = page * P + offset. Bit-exact against the
+ *   float32 IEEE definition above (no FMA contraction, no denormal flush).
+ *
+ * Pool layout (vLLM-style pages; K and V have separate pools):
+ *   codes  uint8   [N_pg][P][H][D/2]   (a token's H rows are contiguous)
+ *   scales float16 [N_pg][P][H]
+ * Slot s addresses row s of the flat [N_pg*P][H][...] view.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or synchronises, keeps no state between calls
+ *     and is safe to call from several host threads.
+ *   - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream)
+ *     and return. Faults in device memory surface at the caller's next
+ *     synchronisation.
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     error nothing is launched and a status > 0 is returned, with detail
+ *     text from sawkv_last_error().
+ *   - A slot < 0 or >= N_pg*P is skipped by append and yields a zero row in
+ *     gather (no byte outside the addressed rows is ever touched).
+ *   - Caller preconditions not checked: no two tokens of one call share a
+ *     slot (which write wins is then unspecified); inputs, outputs and pools
+ *     do not overlap; K/V values are finite.
+ *   - Supported sizes: D = 128; h in {16, 32, 64, 128}; H >= 1; T*H < 2^31.
+ *   - Alignment: every tensor pointer 16-byte aligned, slot_mapping 8-byte
+ *     aligned, token strides multiples of 8 elements.
+ */
+#ifndef SAWKV_H
+#define SAWKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAWKV_VERSION 1
+
+enum {
+  SAWKV_OK = 0,
+  SAWKV_EINVAL = 1,        /* null pointer, negative or inconsistent size   */
+  SAWKV_EUNSUPPORTED = 2,  /* D or h outside the supported set              */
+  SAWKV_EALIGN = 3,        /* pointer or stride misaligned                  */
+  SAWKV_EHIP = 4           /* the HIP runtime refused the launch            */
+};
+
+enum {
+  SAWKV_ROT_NONE = 0,      /* naive token-wise INT4 for K and V             */
+  SAWKV_ROT_K = 1,         /* rotate K only; V is naive INT4                */
+  SAWKV_ROT_KV = 2         /* rotate K and V                                */
+};
+
+/*
+ * Quantise T new tokens of K and V and append them to the paged INT4 pools.
+ * (The fused rotation-quantisation-append kernel of the youngju.dev diagram
+ * and of the gist.science summary, §2 BDR item 3 and §3 item 3.)
+ *
+ *   k, v          fp16 [T][H][D]; row (token) t starts at k + t*k_stride
+ *                 elements; k_stride, v_stride >= H*D. Either k or v may be
+ *                 NULL to skip that tensor (its pool pointers are then
+ *                 ignored); not both.
+ *   slot_mapping  int64 [T], device memory.
+ *   k_codes, v_codes    uint8 [N_pg][P][H][D/2]   (written at mapped rows only)
+ *   k_scales, v_scales  fp16  [N_pg][P][H]
+ *   h             Hadamard block size; rot_mode one of SAWKV_ROT_*.
+ * Returns SAWKV_OK or an error status (nothing launched on error).
+ */
+int sawkv_quantize_append(const void* k, const void* v,
+                          int64_t k_stride, int64_t v_stride,
+                          const int64_t* slot_mapping, int64_t T,
+                          int32_t H, int32_t D,
+                          void* k_codes, void* v_codes,
+                          void* k_scales, void* v_scales,
+                          int64_t N_pg, int32_t P,
+                          int32_t h, int32_t rot_mode,
+                          void* stream);
+
+/*
+ * Read the tokens at slot_mapping back from the pools: y = q * s, then (for
+ * rotated tensors) the same normalised Sylvester transform, which is its own
+ * inverse (youngju.dev reading, "The Rotation Trick": the rotation is
+ * orthogonal and can be undone), then fp16 round-to-nearest-even.
+ *
+ *   k_out, v_out  fp16 [T][H][D] contiguous; a NULL pair (pool and output)
+ *                 skips that tensor; invalid slots give zero rows.
+ * The read-back is exact up to the final f16 rounding: every partial sum of
+ * q * s fits float32, so the result does not depend on summation order.
+ */
+int sawkv_dequant_gather(const void* k_codes, const void* v_codes,
+                         const void* k_scales, const void* v_scales,
+                         int64_t N_pg, int32_t P,
+                         const int64_t* slot_mapping, int64_t T,
+                         int32_t H, int32_t D,
+                         void* k_out, void* v_out,
+                         int32_t h, int32_t rot_mode,
+                         void* stream);
+
+/*
+ * The no-rotation control ("naive" INT4 of the youngju.dev reading, section
+ * "Why Naive INT4 Breaks"; the pure-INT4 throughput baseline of gist.science
+ * §4): the same bytes, launch geometry and semantics as the two calls above
+ * with rot_mode = SAWKV_ROT_NONE, built as separate kernel instantiations.
+ */
+int sawkv_naive_int4_append(const void* k, const void* v,
+                            int64_t k_stride, int64_t v_stride,
+                            const int64_t* slot_mapping, int64_t T,
+                            int32_t H, int32_t D,
+                            void* k_codes, void* v_codes,
+                            void* k_scales, void* v_scales,
+                            int64_t N_pg, int32_t P,
+                            void* stream);
+
+int sawkv_naive_int4_gather(const void* k_codes, const void* v_codes,
+                            const void* k_scales, const void* v_scales,
+                            int64_t N_pg, int32_t P,
+                            const int64_t* slot_mapping, int64_t T,
+                            int32_t H, int32_t D,
+                            void* k_out, void* v_out,
+                            void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* sawkv_status_string(int status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* sawkv_last_error(void);
+
+/* SAWKV_VERSION of the built library. */
+int sawkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAWKV_H */

@@ -1,0 +1,452 @@
+// sawkv: fused block-diagonal Hadamard + token-wise INT4 paged-KV append and
+// its read-back, for MI355X (gfx950). C ABI declared in include/sawkv.h.
+//
+// The method (youngju.dev reading of the SAW-INT4 preprint, fused-kernel
+// diagram in "The System Is the Design - A Fused Kernel"; gist.science
+// summary of SAW-INT4, §2 Metodologia, BDR items 1-3): each new token's fp16
+// K/V head vector is rotated by a block-diagonal Hadamard transform,
+// quantised to INT4 with one scale of its own, and written to its slot of a
+// paged cache in one pass that reads the input once and touches nothing else.
+//
+// Build: hipcc --offload-arch=gfx950 -O3 -ffp-contract=off
+//        -Xclang -target-feature -Xclang -packed-fp32-ops
+// (-ffp-contract=off keeps every float32 operation separately rounded, as the
+// definition requires; fused multiply-adds appear only where written).
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "sawkv.h"
+#include "sawkv_device.hpp"
+
+namespace sawkv {
+
+// ---------------------------------------------------------------------------
+// append: fp16 K/V -> rotate -> token-wise INT4 -> paged pool
+// ---------------------------------------------------------------------------
+
+struct AppendTensor {
+  const __half* src;     // [T][H][D], row stride `stride` elements
+  int64_t stride;
+  uint8_t* codes;        // [n_slots][H][D/2]
+  __half* scales;        // [n_slots][H]
+};
+
+struct AppendParams {
+  AppendTensor t[2];     // blockIdx.y selects the tensor
+  const int64_t* slots;  // [T]
+  int64_t n_slots;       // N_pg * P
+  int32_t TH;            // T * H vectors per tensor
+  int32_t H;
+};
+
+// y = float32 input, or f32(c_h * F_h(x)) with the lane's sign removed.
+// HB == 0: no rotation (naive INT4).
+template <int HB>
+__device__ __forceinline__ void load_transform(const uint4 (&raw)[4], float (&y)[kElems],
+                                               int lam) {
+  if constexpr (HB == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const __half2 hv = __builtin_bit_cast(__half2, w[m]);
+        y[8 * i + 2 * m] = __low2float(hv);
+        y[8 * i + 2 * m + 1] = __high2float(hv);
+      }
+    }
+  } else {
+    // stride-1 butterflies straight from the fp16 pairs: fma(b, 1, a) = f32(a + b)
+    // and fma(b, -1, a) = f32(a - b), one mixed-precision fma each
+    const float one = opaque(1.0f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const __half2 hv = __builtin_bit_cast(__half2, w[m]);
+        const float a = __low2float(hv), b = __high2float(hv);
+        y[8 * i + 2 * m] = __builtin_fmaf(b, one, a);
+        y[8 * i + 2 * m + 1] = __builtin_fmaf(b, -one, a);
+      }
+    }
+    const float sgn = fwht_rest<HB>(y, lam);
+    const float csg = c_h<HB>() * sgn;
+#pragma unroll
+    for (int k = 0; k < kElems; ++k) y[k] = y[k] * csg;
+  }
+}
+
+template <int HB>
+__device__ __forceinline__ void append_one(const AppendTensor& A, const AppendParams& p) {
+  const int lane = threadIdx.x & 63;
+  const int lam = lane & 3;
+  int v = (blockIdx.x * kWaves + (threadIdx.x >> 6)) * kVecPerWave + (lane >> 2);
+  const bool in_range = v < p.TH;
+  if (!in_range) v = p.TH - 1;            // compute on a valid vector, store nothing
+  const int t = (int)((uint32_t)v / (uint32_t)p.H);
+  const int head = v - t * p.H;
+  const int64_t slot = p.slots[t];
+  const bool store = in_range && slot >= 0 && slot < p.n_slots;
+
+  const __half* src = A.src + (int64_t)t * A.stride + head * kD + 8 * lam;
+  uint4 raw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) raw[i] = *reinterpret_cast<const uint4*>(src + 32 * i);
+
+  float y[kElems];
+  load_transform<HB>(raw, y, lam);
+
+  // token-wise scale: amax over the 128 channels of the vector (4 lanes)
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kElems; ++k) m = fmaxf(m, fabsf(y[k]));
+  m = fmaxf(m, quad_xor1(m));
+  m = fmaxf(m, quad_xor2(m));
+  const float s32 = m / 7.0f;                         // IEEE division
+  const __half s16 = __float2half_rn(fminf(s32, 65504.0f));   // RNE, saturating
+  const float sf = __half2float(s16);
+  const float r = sf > 0.0f ? 1.0f / sf : 0.0f;       // IEEE reciprocal
+  // clamp to [-8, 7] can bite only for a saturated or an f16-subnormal scale
+  const bool need_clamp = (s32 > 65504.0f) || (sf < 6.103515625e-05f);
+
+  // q = rint(f32(y / s)): Markstein's correction of y * RN(1/s) gives the
+  // correctly rounded quotient (residual by fma, exact); adding 1.5*2^23 + 8
+  // then rounds to an integer half-to-even and leaves q + 8 in the low bits.
+  uint32_t u[kElems];
+#pragma unroll
+  for (int k = 0; k < kElems; ++k) {
+    const float q0 = y[k] * r;
+    const float e = __builtin_fmaf(-q0, sf, y[k]);
+    const float q1 = __builtin_fmaf(e, r, q0);
+    u[k] = __builtin_bit_cast(uint32_t, q1 + 12582920.0f);
+  }
+  if (__any(need_clamp)) {
+#pragma unroll
+    for (int k = 0; k < kElems; ++k) u[k] = min(max(u[k], 0x4B400000u), 0x4B40000Fu);
+  }
+
+  // pack: byte b of chunk i = (q_{2b} & 15) | (q_{2b+1} & 15) << 4; nibbles
+  // hold q + 8 until the final xor with 0x8 per nibble
+  uint32_t d[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t* w = u + 8 * i;
+    const uint32_t p01 = (w[1] << 4) | w[0];    // byte 0 valid, byte 1 zero
+    const uint32_t p23 = (w[3] << 4) | w[2];
+    const uint32_t p45 = (w[5] << 4) | w[4];
+    const uint32_t p67 = (w[7] << 4) | w[6];
+    const uint32_t lo = (p23 << 8) | p01;       // bytes 0-1 valid
+    const uint32_t hi = (p67 << 8) | p45;
+    d[i] = __builtin_amdgcn_perm(hi, lo, 0x05040100u) ^ 0x88888888u;
+  }
+
+  if (store) {
+    const int64_t row = slot * p.H + head;
+    uint8_t* dst = A.codes + row * (kD / 2) + 4 * lam;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(dst + 16 * i) = d[i];
+    if (lam == 0) A.scales[row] = s16;
+  }
+}
+
+template <int HB0, int HB1>
+__global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p) {
+  if (blockIdx.y == 0) append_one<HB0>(p.t[0], p);
+  else append_one<HB1>(p.t[1], p);
+}
+
+// ---------------------------------------------------------------------------
+// gather: pool -> dequantise -> inverse rotation -> fp16
+// ---------------------------------------------------------------------------
+
+struct GatherTensor {
+  const uint8_t* codes;  // [n_slots][H][D/2]
+  const __half* scales;  // [n_slots][H]
+  __half* out;           // [T][H][D]
+};
+
+struct GatherParams {
+  GatherTensor t[2];
+  const int64_t* slots;
+  int64_t n_slots;
+  int32_t TH;
+  int32_t H;
+};
+
+template <int HB>
+__device__ __forceinline__ void gather_one(const GatherTensor& G, const GatherParams& p) {
+  const int lane = threadIdx.x & 63;
+  const int lam = lane & 3;
+  int v = (blockIdx.x * kWaves + (threadIdx.x >> 6)) * kVecPerWave + (lane >> 2);
+  const bool in_range = v < p.TH;
+  if (!in_range) v = p.TH - 1;
+  const int t = (int)((uint32_t)v / (uint32_t)p.H);
+  const int head = v - t * p.H;
+  const int64_t slot = p.slots[t];
+  const bool valid = slot >= 0 && slot < p.n_slots;
+
+  uint32_t d[4] = {0u, 0u, 0u, 0u};
+  float sf = 0.0f;
+  if (valid) {
+    const int64_t row = slot * p.H + head;
+    const uint8_t* src = G.codes + row * (kD / 2) + 4 * lam;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = *reinterpret_cast<const uint32_t*>(src + 16 * i);
+    sf = __half2float(G.scales[row]);
+  }
+
+  // integer codes; every butterfly partial sum is an integer of magnitude
+  // <= 1024, so the transform is exact in float32 and its order is immaterial
+  float x[kElems];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      x[8 * i + j] = (float)__builtin_amdgcn_sbfe((int)d[i], 4 * j, 4);
+
+  float o[kElems];
+  if constexpr (HB == 0) {
+#pragma unroll
+    for (int k = 0; k < kElems; ++k) o[k] = x[k] * sf;     // exact
+  } else {
+    lane_stage<0>(x);
+    const float sgn = fwht_rest<HB>(x, lam);
+    const float csg = c_h<HB>() * sgn;
+    // (F q) * s is exact; one rounding for * c_h; the + 0 turns a -0 that the
+    // sign bookkeeping may leave on an exact zero into +0
+#pragma unroll
+    for (int k = 0; k < kElems; ++k) o[k] = __builtin_fmaf(x[k] * sf, csg, 0.0f);
+  }
+
+  if (in_range) {
+    __half* dst = G.out + (int64_t)v * kD + 8 * lam;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint4 w;
+      w.x = __builtin_bit_cast(uint32_t, __floats2half2_rn(o[8 * i + 0], o[8 * i + 1]));
+      w.y = __builtin_bit_cast(uint32_t, __floats2half2_rn(o[8 * i + 2], o[8 * i + 3]));
+      w.z = __builtin_bit_cast(uint32_t, __floats2half2_rn(o[8 * i + 4], o[8 * i + 5]));
+      w.w = __builtin_bit_cast(uint32_t, __floats2half2_rn(o[8 * i + 6], o[8 * i + 7]));
+      *reinterpret_cast<uint4*>(dst + 32 * i) = w;
+    }
+  }
+}
+
+template <int HB0, int HB1>
+__global__ __launch_bounds__(kThreads) void gather_kernel(GatherParams p) {
+  if (blockIdx.y == 0) gather_one<HB0>(p.t[0], p);
+  else gather_one<HB1>(p.t[1], p);
+}
+
+}  // namespace sawkv
+
+// ---------------------------------------------------------------------------
+// host side: validation, dispatch, C ABI
+// ---------------------------------------------------------------------------
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return SAWKV_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_geometry(int64_t T, int32_t H, int32_t D, int64_t N_pg, int32_t P, int32_t h,
+                   int32_t rot_mode, const int64_t* slots) {
+  if (T < 0) return fail(SAWKV_EINVAL, "T = %lld is negative", (long long)T);
+  if (H <= 0) return fail(SAWKV_EINVAL, "H = %d must be positive", H);
+  if (D != sawkv::kD) return fail(SAWKV_EUNSUPPORTED, "D = %d unsupported (only 128)", D);
+  if (P <= 0) return fail(SAWKV_EINVAL, "P = %d must be positive", P);
+  if (N_pg <= 0) return fail(SAWKV_EINVAL, "N_pg = %lld must be positive", (long long)N_pg);
+  if (N_pg > (INT64_C(1) << 40) / P || N_pg * P > (INT64_C(1) << 56) / ((int64_t)H * D))
+    return fail(SAWKV_EINVAL, "pool of %lld pages x %d slots is too large", (long long)N_pg, P);
+  if (h != 16 && h != 32 && h != 64 && h != 128)
+    return fail(SAWKV_EUNSUPPORTED, "h = %d unsupported (16, 32, 64 or 128)", h);
+  if (h > D) return fail(SAWKV_EUNSUPPORTED, "h = %d exceeds D = %d", h, D);
+  if (rot_mode != SAWKV_ROT_NONE && rot_mode != SAWKV_ROT_K && rot_mode != SAWKV_ROT_KV)
+    return fail(SAWKV_EINVAL, "rot_mode = %d invalid", rot_mode);
+  if (T * (int64_t)H >= (INT64_C(1) << 31))
+    return fail(SAWKV_EUNSUPPORTED, "T*H = %lld too large (< 2^31)", (long long)(T * H));
+  if (slots == nullptr) return fail(SAWKV_EINVAL, "slot_mapping is NULL");
+  if (!aligned(slots, 8)) return fail(SAWKV_EALIGN, "slot_mapping not 8-byte aligned");
+  return SAWKV_OK;
+}
+
+int check_tensor(const char* name, const void* x, int64_t stride, const void* codes,
+                 const void* scales, int32_t H, int32_t D) {
+  if (codes == nullptr || scales == nullptr)
+    return fail(SAWKV_EINVAL, "%s pool pointer is NULL", name);
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 16))
+    return fail(SAWKV_EALIGN, "%s tensor or pool pointer not 16-byte aligned", name);
+  if (stride >= 0) {
+    if (stride < (int64_t)H * D)
+      return fail(SAWKV_EINVAL, "%s stride %lld < H*D = %d", name, (long long)stride, H * D);
+    if (stride % 8 != 0)
+      return fail(SAWKV_EALIGN, "%s stride %lld not a multiple of 8", name, (long long)stride);
+  }
+  return SAWKV_OK;
+}
+
+// kernel index: 0 = naive, 1..4 = h 16/32/64/128
+int hb_index(int32_t h, bool rot) {
+  if (!rot) return 0;
+  return h == 16 ? 1 : h == 32 ? 2 : h == 64 ? 3 : 4;
+}
+
+// Instantiated pairs (tensor 0, tensor 1): both naive, rotated + naive (keys
+// only, or a single rotated tensor), both rotated with the same h.
+#define SAWKV_TABLE(K)                                                              \
+  {{(void*)&K<0, 0>, nullptr, nullptr, nullptr, nullptr},                           \
+   {(void*)&K<16, 0>, (void*)&K<16, 16>, nullptr, nullptr, nullptr},                \
+   {(void*)&K<32, 0>, nullptr, (void*)&K<32, 32>, nullptr, nullptr},                \
+   {(void*)&K<64, 0>, nullptr, nullptr, (void*)&K<64, 64>, nullptr},                \
+   {(void*)&K<128, 0>, nullptr, nullptr, nullptr, (void*)&K<128, 128>}}
+
+const void* const kAppend[5][5] = SAWKV_TABLE(sawkv::append_kernel);
+const void* const kGather[5][5] = SAWKV_TABLE(sawkv::gather_kernel);
+
+#undef SAWKV_TABLE
+
+int launch(const void* fn, int ntensors, int32_t TH, void* params, void* stream) {
+  if (fn == nullptr) return fail(SAWKV_EINVAL, "no kernel for this tensor/rotation combination");
+  const dim3 grid((unsigned)((TH + sawkv::kVecPerBlock - 1) / sawkv::kVecPerBlock),
+                  (unsigned)ntensors);
+  void* args[] = {params};
+  const hipError_t e = hipLaunchKernel(fn, grid, dim3(sawkv::kThreads), args, 0,
+                                       reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SAWKV_EHIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int append_impl(const void* k, const void* v, int64_t k_stride, int64_t v_stride,
+                const int64_t* slots, int64_t T, int32_t H, int32_t D, void* k_codes,
+                void* v_codes, void* k_scales, void* v_scales, int64_t N_pg, int32_t P,
+                int32_t h, int32_t rot_mode, void* stream) {
+  int st = check_geometry(T, H, D, N_pg, P, h, rot_mode, slots);
+  if (st) return st;
+  if (k == nullptr && v == nullptr) return fail(SAWKV_EINVAL, "both k and v are NULL");
+  if (k && (st = check_tensor("k", k, k_stride, k_codes, k_scales, H, D))) return st;
+  if (v && (st = check_tensor("v", v, v_stride, v_codes, v_scales, H, D))) return st;
+  if (T == 0) return ok();
+
+  sawkv::AppendParams p{};
+  int n = 0, hb[2] = {0, 0};
+  if (k) {
+    p.t[n] = {static_cast<const __half*>(k), k_stride, static_cast<uint8_t*>(k_codes),
+              static_cast<__half*>(k_scales)};
+    hb[n++] = hb_index(h, rot_mode != SAWKV_ROT_NONE);
+  }
+  if (v) {
+    p.t[n] = {static_cast<const __half*>(v), v_stride, static_cast<uint8_t*>(v_codes),
+              static_cast<__half*>(v_scales)};
+    hb[n++] = hb_index(h, rot_mode == SAWKV_ROT_KV);
+  }
+  p.slots = slots;
+  p.n_slots = N_pg * P;
+  p.TH = (int32_t)(T * H);
+  p.H = H;
+  return launch(kAppend[hb[0]][hb[1]], n, p.TH, &p, stream);
+}
+
+int gather_impl(const void* k_codes, const void* v_codes, const void* k_scales,
+                const void* v_scales, int64_t N_pg, int32_t P, const int64_t* slots,
+                int64_t T, int32_t H, int32_t D, void* k_out, void* v_out, int32_t h,
+                int32_t rot_mode, void* stream) {
+  int st = check_geometry(T, H, D, N_pg, P, h, rot_mode, slots);
+  if (st) return st;
+  if (k_out == nullptr && v_out == nullptr) return fail(SAWKV_EINVAL, "both outputs are NULL");
+  if (k_out && (st = check_tensor("k", k_out, -1, k_codes, k_scales, H, D))) return st;
+  if (v_out && (st = check_tensor("v", v_out, -1, v_codes, v_scales, H, D))) return st;
+  if (T == 0) return ok();
+
+  sawkv::GatherParams p{};
+  int n = 0, hb[2] = {0, 0};
+  if (k_out) {
+    p.t[n] = {static_cast<const uint8_t*>(k_codes), static_cast<const __half*>(k_scales),
+              static_cast<__half*>(k_out)};
+    hb[n++] = hb_index(h, rot_mode != SAWKV_ROT_NONE);
+  }
+  if (v_out) {
+    p.t[n] = {static_cast<const uint8_t*>(v_codes), static_cast<const __half*>(v_scales),
+              static_cast<__half*>(v_out)};
+    hb[n++] = hb_index(h, rot_mode == SAWKV_ROT_KV);
+  }
+  p.slots = slots;
+  p.n_slots = N_pg * P;
+  p.TH = (int32_t)(T * H);
+  p.H = H;
+  return launch(kGather[hb[0]][hb[1]], n, p.TH, &p, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int sawkv_quantize_append(const void* k, const void* v, int64_t k_stride, int64_t v_stride,
+                          const int64_t* slot_mapping, int64_t T, int32_t H, int32_t D,
+                          void* k_codes, void* v_codes, void* k_scales, void* v_scales,
+                          int64_t N_pg, int32_t P, int32_t h, int32_t rot_mode,
+                          void* stream) {
+  return append_impl(k, v, k_stride, v_stride, slot_mapping, T, H, D, k_codes, v_codes,
+                     k_scales, v_scales, N_pg, P, h, rot_mode, stream);
+}
+
+int sawkv_dequant_gather(const void* k_codes, const void* v_codes, const void* k_scales,
+                         const void* v_scales, int64_t N_pg, int32_t P,
+                         const int64_t* slot_mapping, int64_t T, int32_t H, int32_t D,
+                         void* k_out, void* v_out, int32_t h, int32_t rot_mode,
+                         void* stream) {
+  return gather_impl(k_codes, v_codes, k_scales, v_scales, N_pg, P, slot_mapping, T, H, D,
+                     k_out, v_out, h, rot_mode, stream);
+}
+
+int sawkv_naive_int4_append(const void* k, const void* v, int64_t k_stride, int64_t v_stride,
+                            const int64_t* slot_mapping, int64_t T, int32_t H, int32_t D,
+                            void* k_codes, void* v_codes, void* k_scales, void* v_scales,
+                            int64_t N_pg, int32_t P, void* stream) {
+  return append_impl(k, v, k_stride, v_stride, slot_mapping, T, H, D, k_codes, v_codes,
+                     k_scales, v_scales, N_pg, P, 128, SAWKV_ROT_NONE, stream);
+}
+
+int sawkv_naive_int4_gather(const void* k_codes, const void* v_codes, const void* k_scales,
+                            const void* v_scales, int64_t N_pg, int32_t P,
+                            const int64_t* slot_mapping, int64_t T, int32_t H, int32_t D,
+                            void* k_out, void* v_out, void* stream) {
+  return gather_impl(k_codes, v_codes, k_scales, v_scales, N_pg, P, slot_mapping, T, H, D,
+                     k_out, v_out, 128, SAWKV_ROT_NONE, stream);
+}
+
+const char* sawkv_status_string(int status) {
+  switch (status) {
+    case SAWKV_OK: return "ok";
+    case SAWKV_EINVAL: return "invalid argument";
+    case SAWKV_EUNSUPPORTED: return "unsupported size";
+    case SAWKV_EALIGN: return "misaligned pointer or stride";
+    case SAWKV_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* sawkv_last_error(void) { return g_err; }
+
+int sawkv_version(void) { return SAWKV_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,189 @@
+"""Thin ctypes binding over libsawkv.so (C ABI in include/sawkv.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library. Tensors are torch tensors on the ROCm device; torch
+provides the memory and the current stream. Importing this module loads the
+library and raises ImportError when it has not been built
+(python -m int4_kv_cache_amd.build).
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsawkv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m int4_kv_cache_amd.build`")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+OK, EINVAL, EUNSUPPORTED, EALIGN, EHIP = 0, 1, 2, 3, 4
+ROT_NONE, ROT_K, ROT_KV = 0, 1, 2
+ROT = {"none": ROT_NONE, "k": ROT_K, "kv": ROT_KV}
+
+_p, _i64, _i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+
+lib.sawkv_quantize_append.argtypes = [_p, _p, _i64, _i64, _p, _i64, _i32, _i32,
+                                      _p, _p, _p, _p, _i64, _i32, _i32, _i32, _p]
+lib.sawkv_quantize_append.restype = ctypes.c_int
+lib.sawkv_dequant_gather.argtypes = [_p, _p, _p, _p, _i64, _i32, _p, _i64, _i32, _i32,
+                                     _p, _p, _i32, _i32, _p]
+lib.sawkv_dequant_gather.restype = ctypes.c_int
+lib.sawkv_naive_int4_append.argtypes = [_p, _p, _i64, _i64, _p, _i64, _i32, _i32,
+                                        _p, _p, _p, _p, _i64, _i32, _p]
+lib.sawkv_naive_int4_append.restype = ctypes.c_int
+lib.sawkv_naive_int4_gather.argtypes = [_p, _p, _p, _p, _i64, _i32, _p, _i64, _i32, _i32,
+                                        _p, _p, _p]
+lib.sawkv_naive_int4_gather.restype = ctypes.c_int
+lib.sawkv_status_string.argtypes = [ctypes.c_int]
+lib.sawkv_status_string.restype = ctypes.c_char_p
+lib.sawkv_last_error.argtypes = []
+lib.sawkv_last_error.restype = ctypes.c_char_p
+lib.sawkv_version.argtypes = []
+lib.sawkv_version.restype = ctypes.c_int
+
+
+class SawkvError(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__(f"sawkv status {status} ({lib.sawkv_status_string(status).decode()}): "
+                         f"{detail}")
+
+
+def _check(status):
+    if status != OK:
+        raise SawkvError(status, lib.sawkv_last_error().decode())
+
+
+def _addr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _rot(rot):
+    return ROT[rot] if isinstance(rot, str) else int(rot)
+
+
+def _kv_geometry(x):
+    """[T, H, D] fp16 view with unit channel stride and head stride D; returns
+    (T, H, D, token stride in elements)."""
+    if x.dtype != torch.float16 or x.dim() != 3:
+        raise ValueError("K/V must be fp16 [T, H, D]")
+    T, H, D = x.shape
+    if x.stride(2) != 1 or (H > 1 and x.stride(1) != D):
+        raise ValueError("K/V must have unit channel stride and head stride D")
+    return T, H, D, x.stride(0)
+
+
+def _pool_geometry(codes, scales):
+    if codes.dtype != torch.uint8 or codes.dim() != 4 or not codes.is_contiguous():
+        raise ValueError("codes must be contiguous uint8 [N_pg, P, H, D/2]")
+    if scales.dtype != torch.float16 or tuple(scales.shape) != tuple(codes.shape[:3]) \
+            or not scales.is_contiguous():
+        raise ValueError("scales must be contiguous fp16 [N_pg, P, H]")
+    return codes.shape
+
+
+def alloc_pools(N_pg, P, H, D, device="cuda", code_fill=None, scale_bits_fill=None):
+    """The four pool tensors (K codes, V codes, K scales, V scales)."""
+    kc = torch.empty((N_pg, P, H, D // 2), dtype=torch.uint8, device=device)
+    vc = torch.empty_like(kc)
+    ks = torch.empty((N_pg, P, H), dtype=torch.float16, device=device)
+    vs = torch.empty_like(ks)
+    if code_fill is not None:
+        kc.fill_(code_fill)
+        vc.fill_(code_fill)
+    if scale_bits_fill is not None:
+        ks.view(torch.int16).fill_(scale_bits_fill)
+        vs.view(torch.int16).fill_(scale_bits_fill)
+    return kc, vc, ks, vs
+
+
+def quantize_append(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, *,
+                    h=128, rot="kv", stream=None):
+    """Fused rotate + token-wise INT4 + paged append (sawkv_quantize_append).
+    k or v may be None to skip that tensor."""
+    ref = k if k is not None else v
+    T, H, D, _ = _kv_geometry(ref)
+    ks_ = _kv_geometry(k)[3] if k is not None else 0
+    vs_ = _kv_geometry(v)[3] if v is not None else 0
+    pool = _pool_geometry(k_codes, k_scales) if k is not None else \
+        _pool_geometry(v_codes, v_scales)
+    N_pg, P = pool[0], pool[1]
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must be int64 [T]")
+    _check(lib.sawkv_quantize_append(
+        _addr(k), _addr(v), ks_, vs_, _addr(slot_mapping), T, H, D,
+        _addr(k_codes) if k is not None else None, _addr(v_codes) if v is not None else None,
+        _addr(k_scales) if k is not None else None, _addr(v_scales) if v is not None else None,
+        N_pg, P, h, _rot(rot), _stream(stream)))
+
+
+def naive_int4_append(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, *,
+                      stream=None):
+    """The no-rotation control (sawkv_naive_int4_append)."""
+    ref = k if k is not None else v
+    T, H, D, _ = _kv_geometry(ref)
+    ks_ = _kv_geometry(k)[3] if k is not None else 0
+    vs_ = _kv_geometry(v)[3] if v is not None else 0
+    pool = _pool_geometry(k_codes, k_scales) if k is not None else \
+        _pool_geometry(v_codes, v_scales)
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must be int64 [T]")
+    _check(lib.sawkv_naive_int4_append(
+        _addr(k), _addr(v), ks_, vs_, _addr(slot_mapping), T, H, D,
+        _addr(k_codes) if k is not None else None, _addr(v_codes) if v is not None else None,
+        _addr(k_scales) if k is not None else None, _addr(v_scales) if v is not None else None,
+        pool[0], pool[1], _stream(stream)))
+
+
+def _gather_args(k_codes, v_codes, k_scales, v_scales, slot_mapping, k_out, v_out, want_k,
+                 want_v):
+    pool = _pool_geometry(k_codes, k_scales) if want_k else _pool_geometry(v_codes, v_scales)
+    N_pg, P, H, half = pool
+    D = 2 * half
+    T = slot_mapping.numel()
+    if slot_mapping.dtype != torch.int64:
+        raise ValueError("slot_mapping must be int64 [T]")
+    dev = (k_codes if want_k else v_codes).device
+    if want_k and k_out is None:
+        k_out = torch.empty((T, H, D), dtype=torch.float16, device=dev)
+    if want_v and v_out is None:
+        v_out = torch.empty((T, H, D), dtype=torch.float16, device=dev)
+    for o in (k_out, v_out):
+        if o is not None and (o.dtype != torch.float16 or tuple(o.shape) != (T, H, D)
+                              or not o.is_contiguous()):
+            raise ValueError("outputs must be contiguous fp16 [T, H, D]")
+    return N_pg, P, H, D, T, (k_out if want_k else None), (v_out if want_v else None)
+
+
+def dequant_gather(k_codes, v_codes, k_scales, v_scales, slot_mapping, *, h=128, rot="kv",
+                   k_out=None, v_out=None, want_k=True, want_v=True, stream=None):
+    """Dequantise + inverse-rotate the slots back to fp16 (sawkv_dequant_gather).
+    Returns (k_out, v_out); a tensor not wanted is None."""
+    N_pg, P, H, D, T, k_out, v_out = _gather_args(k_codes, v_codes, k_scales, v_scales,
+                                                  slot_mapping, k_out, v_out, want_k, want_v)
+    _check(lib.sawkv_dequant_gather(
+        _addr(k_codes) if want_k else None, _addr(v_codes) if want_v else None,
+        _addr(k_scales) if want_k else None, _addr(v_scales) if want_v else None,
+        N_pg, P, _addr(slot_mapping), T, H, D, _addr(k_out), _addr(v_out), h, _rot(rot),
+        _stream(stream)))
+    return k_out, v_out
+
+
+def naive_int4_gather(k_codes, v_codes, k_scales, v_scales, slot_mapping, *, k_out=None,
+                      v_out=None, want_k=True, want_v=True, stream=None):
+    N_pg, P, H, D, T, k_out, v_out = _gather_args(k_codes, v_codes, k_scales, v_scales,
+                                                  slot_mapping, k_out, v_out, want_k, want_v)
+    _check(lib.sawkv_naive_int4_gather(
+        _addr(k_codes) if want_k else None, _addr(v_codes) if want_v else None,
+        _addr(k_scales) if want_k else None, _addr(v_scales) if want_v else None,
+        N_pg, P, _addr(slot_mapping), T, H, D, _addr(k_out), _addr(v_out), _stream(stream)))
+    return k_out, v_out

@@ -1,0 +1,145 @@
+"""The C ABI of libsawkv.so on the host (CPU only, no GPU).
+
+Every call here either fails host-side validation or has T == 0, so nothing
+is ever launched: validation runs before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sawkv.h")
+LIB = os.path.join(ROOT, "int4_kv_cache_amd", "libsawkv.so")
+
+OK, EINVAL, EUNSUPPORTED, EALIGN, EHIP = 0, 1, 2, 3, 4
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libsawkv.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sawkv_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    L = ctypes.CDLL(LIB)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    L.sawkv_quantize_append.argtypes = [p, p, i64, i64, p, i64, i32, i32, p, p, p, p, i64, i32,
+                                        i32, i32, p]
+    L.sawkv_dequant_gather.argtypes = [p, p, p, p, i64, i32, p, i64, i32, i32, p, p, i32, i32, p]
+    L.sawkv_naive_int4_append.argtypes = [p, p, i64, i64, p, i64, i32, i32, p, p, p, p, i64,
+                                          i32, p]
+    L.sawkv_naive_int4_gather.argtypes = [p, p, p, p, i64, i32, p, i64, i32, i32, p, p, p]
+    L.sawkv_status_string.restype = ctypes.c_char_p
+    L.sawkv_last_error.restype = ctypes.c_char_p
+    return L
+
+
+def test_header_symbols_exported(lib):
+    names = declared_functions()
+    assert set(names) >= {"sawkv_quantize_append", "sawkv_dequant_gather",
+                          "sawkv_naive_int4_append", "sawkv_naive_int4_gather",
+                          "sawkv_status_string", "sawkv_last_error", "sawkv_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.sawkv_version() == 1
+    for st, word in ((OK, b"ok"), (EINVAL, b"invalid"), (EUNSUPPORTED, b"unsupported"),
+                     (EALIGN, b"misaligned"), (EHIP, b"HIP")):
+        assert word in lib.sawkv_status_string(st)
+    assert lib.sawkv_status_string(99) == b"unknown status"
+
+
+# fake, suitably aligned addresses: never dereferenced, because every call
+# below stops in validation or has T == 0
+A = 0x100000
+K, V, S, KC, VC, KS, VS = (A * i for i in range(1, 8))
+
+
+def app(lib, **kw):
+    a = dict(k=K, v=V, ks=1024, vs=1024, slots=S, T=64, H=8, D=128, kc=KC, vc=VC, kss=KS,
+             vss=VS, npg=16, P=16, h=128, rot=2)
+    a.update(kw)
+    return lib.sawkv_quantize_append(a["k"], a["v"], a["ks"], a["vs"], a["slots"], a["T"],
+                                     a["H"], a["D"], a["kc"], a["vc"], a["kss"], a["vss"],
+                                     a["npg"], a["P"], a["h"], a["rot"], None)
+
+
+def gat(lib, **kw):
+    a = dict(kc=KC, vc=VC, kss=KS, vss=VS, npg=16, P=16, slots=S, T=64, H=8, D=128, ko=K,
+             vo=V, h=128, rot=2)
+    a.update(kw)
+    return lib.sawkv_dequant_gather(a["kc"], a["vc"], a["kss"], a["vss"], a["npg"], a["P"],
+                                    a["slots"], a["T"], a["H"], a["D"], a["ko"], a["vo"],
+                                    a["h"], a["rot"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), EINVAL),
+    (dict(H=0), EINVAL),
+    (dict(D=64), EUNSUPPORTED),
+    (dict(D=256), EUNSUPPORTED),
+    (dict(P=0), EINVAL),
+    (dict(npg=0), EINVAL),
+    (dict(npg=1 << 40), EINVAL),
+    (dict(h=48), EUNSUPPORTED),
+    (dict(h=8), EUNSUPPORTED),
+    (dict(h=256), EUNSUPPORTED),
+    (dict(rot=3), EINVAL),
+    (dict(rot=-1), EINVAL),
+    (dict(T=1 << 31, H=1), EUNSUPPORTED),
+    (dict(slots=None), EINVAL),
+    (dict(slots=S + 4), EALIGN),
+    (dict(k=None, v=None), EINVAL),
+    (dict(kc=None), EINVAL),
+    (dict(vss=None), EINVAL),
+    (dict(k=K + 8), EALIGN),
+    (dict(vc=VC + 2), EALIGN),
+    (dict(ks=1000), EINVAL),
+    (dict(vs=1028), EALIGN),
+])
+def test_append_validation(lib, kw, status):
+    assert app(lib, **kw) == status
+    assert lib.sawkv_last_error() != b""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-5), EINVAL),
+    (dict(D=96), EUNSUPPORTED),
+    (dict(h=100), EUNSUPPORTED),
+    (dict(ko=None, vo=None), EINVAL),
+    (dict(kc=None), EINVAL),
+    (dict(ko=K + 4), EALIGN),
+    (dict(rot=7), EINVAL),
+    (dict(slots=None), EINVAL),
+])
+def test_gather_validation(lib, kw, status):
+    assert gat(lib, **kw) == status
+
+
+def test_naive_entry_points_validate(lib):
+    assert lib.sawkv_naive_int4_append(K, V, 1024, 1024, S, 64, 8, 64, KC, VC, KS, VS, 16, 16,
+                                       None) == EUNSUPPORTED
+    assert lib.sawkv_naive_int4_gather(KC, VC, KS, VS, 16, 16, S, 64, 8, 128, None, None,
+                                       None) == EINVAL
+
+
+def test_zero_tokens_launch_nothing(lib):
+    assert app(lib, T=0) == OK
+    assert lib.sawkv_last_error() == b""
+    assert gat(lib, T=0) == OK
+    assert app(lib, T=0, v=None, vc=None, vss=None, rot=1) == OK
+    assert lib.sawkv_naive_int4_append(K, None, 1024, 0, S, 0, 8, 128, KC, None, KS, None, 4,
+                                       16, None) == OK
+
+
+def test_one_tensor_may_be_absent(lib):
+    # V absent: its pool pointers are ignored (T = 0 keeps this launch-free)
+    assert app(lib, T=0, v=None, vc=None, vss=None) == OK
+    assert gat(lib, T=0, ko=None, kc=None, kss=None) == OK

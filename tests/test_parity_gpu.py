@@ -1,0 +1,393 @@
+"""GPU parity: the HIP kernels (called through the C ABI) against the CPU oracle.
+
+Codes and scales must match the oracle byte for byte; gathered fp16 rows must
+match the oracle's read-back byte for byte and, per vector, within 1e-3 of the
+vector's largest magnitude (the tolerance asked of the read path). Small and
+ragged cases compare every byte of the pools; the full-size workloads compare
+seeded samples of tokens element by element, plus pool-wide properties that
+hold at any size (exactly the mapped rows are written).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import sawint4 as O
+from int4_kv_cache_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+SENT_CODE = 0xAA
+SENT_SCALE = 0xFFFF          # an fp16 NaN pattern: never a valid scale
+ROTS = {O.ROT_NONE: "none", O.ROT_K: "k", O.ROT_KV: "kv"}
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm device")
+    from int4_kv_cache_amd import sawkv as S   # raises if libsawkv.so is missing
+    return torch, S
+
+
+def say(*a):
+    print("[gpu]", *a, flush=True)
+    sys.stdout.flush()
+
+
+# --------------------------------------------------------------------------
+# helpers
+# --------------------------------------------------------------------------
+
+def np_pools(n_pg, P, H, D):
+    kc = np.full((n_pg, P, H, D // 2), SENT_CODE, np.uint8)
+    ks = np.full((n_pg, P, H), SENT_SCALE, np.uint16).view(np.float16)
+    return kc, kc.copy(), ks, ks.copy()
+
+
+def gpu_pools(env, n_pg, P, H, D):
+    torch, S = env
+    return S.alloc_pools(n_pg, P, H, D, "cuda", code_fill=SENT_CODE, scale_bits_fill=-1)
+
+
+def to_np(t):
+    return t.detach().cpu().numpy()
+
+
+def assert_pools_equal(got, want, what=""):
+    names = ("k_codes", "v_codes", "k_scales", "v_scales")
+    for name, g, w in zip(names, got, want):
+        g = np.asarray(g)
+        w = np.asarray(w)
+        if g.tobytes() != w.tobytes():
+            gb = g.view(np.uint8).reshape(-1)
+            wb = w.view(np.uint8).reshape(-1)
+            bad = np.nonzero(gb != wb)[0]
+            raise AssertionError(f"{what} {name}: {len(bad)} bytes differ, first at {bad[:8]}")
+
+
+def assert_rows_close(got, want, what=""):
+    """fp16 [N, H, D]: byte-identical, and per vector within 1e-3 of its max."""
+    g = np.asarray(got).astype(np.float64)
+    w = np.asarray(want).astype(np.float64)
+    scale = np.max(np.abs(w), axis=-1, keepdims=True)
+    err = np.max(np.abs(g - w), axis=-1, keepdims=True)
+    assert np.all(err <= 1e-3 * scale), f"{what}: tolerance exceeded, max {np.max(err / np.maximum(scale, 1e-30))}"
+    gb, wb = np.asarray(got).view(np.uint16), np.asarray(want).view(np.uint16)
+    nbad = int(np.sum(gb != wb))
+    assert nbad == 0, f"{what}: {nbad} fp16 values differ in bits"
+
+
+def run_case(env, k, v, slots, n_pg, P, h, rot, gather=True, what=""):
+    """Append (and gather) on the GPU and in the oracle; compare everything."""
+    torch, S = env
+    T, H, D = (k if k is not None else v).shape
+    say(what, f"T={T} H={H} h={h} rot={ROTS[rot]} n_pg={n_pg} P={P}")
+    kd = torch.from_numpy(k).cuda() if k is not None else None
+    vd = torch.from_numpy(v).cuda() if v is not None else None
+    sd = torch.from_numpy(slots).cuda()
+    gp = gpu_pools(env, n_pg, P, H, D)
+    S.quantize_append(kd, vd, sd, *gp, h=h, rot=ROTS[rot])
+    torch.cuda.synchronize()
+    got = [to_np(x) for x in gp]
+    want = np_pools(n_pg, P, H, D)
+    O.quantize_append(k, v, slots, *want, h=h, rot_mode=rot)
+    assert_pools_equal(got, want, what)
+    if gather:
+        ko, vo = S.dequant_gather(*gp, sd, h=h, rot=ROTS[rot], want_k=k is not None,
+                                  want_v=v is not None)
+        torch.cuda.synchronize()
+        rk, rv = O.dequant_gather(*want, slots, h=h, rot_mode=rot)
+        if k is not None:
+            assert_rows_close(to_np(ko), rk, what + " k gather")
+        if v is not None:
+            assert_rows_close(to_np(vo), rv, what + " v gather")
+    return got
+
+
+# --------------------------------------------------------------------------
+# small cases: every byte compared
+# --------------------------------------------------------------------------
+
+def test_tiny_workload_bit_exact(env):
+    wl = W.WORKLOADS["tiny"]
+    k, v = W.kv(wl)
+    slots = W.slot_mapping(wl)
+    got = run_case(env, k, v, slots, wl.N_pg, wl.P, wl.h, wl.rot_mode, what="tiny")
+    # the 4 sentinel pages were never touched
+    assert np.all(got[0][4:] == SENT_CODE) and np.all(got[2][4:].view(np.uint16) == SENT_SCALE)
+
+
+@pytest.mark.parametrize("h", [16, 32, 64, 128])
+@pytest.mark.parametrize("rot", [O.ROT_NONE, O.ROT_K, O.ROT_KV])
+def test_all_block_sizes_and_modes(env, h, rot):
+    wl = W.WORKLOADS["sweep"]
+    T = 1000                                  # 8000 vectors: 125 blocks, ragged tail
+    k, v = W.kv(wl, 0, 0, T)
+    rng = np.random.default_rng(h * 10 + rot)
+    n_pg, P = 80, 16
+    slots = rng.choice(n_pg * P, size=T, replace=False).astype(np.int64)
+    slots[rng.choice(T, 20, replace=False)] = -1
+    slots[rng.choice(T, 5, replace=False)] = n_pg * P + 7     # out of range: skipped
+    run_case(env, k, v, slots, n_pg, P, h, rot, what=f"modes h={h} rot={rot}")
+
+
+@pytest.mark.parametrize("H,T", [(1, 7), (3, 333), (5, 64), (16, 129), (2, 1), (7, 1031)])
+def test_ragged_shapes(env, H, T):
+    rng = np.random.default_rng(H * 1000 + T)
+    k = (rng.standard_normal((T, H, 128)) * 3).astype(np.float16)
+    v = (rng.standard_t(4, (T, H, 128))).astype(np.float16)
+    P = 8
+    n_pg = (T + P - 1) // P + 3
+    slots = rng.permutation(n_pg * P)[:T].astype(np.int64)
+    run_case(env, k, v, slots, n_pg, P, 128, O.ROT_KV, what=f"ragged H={H} T={T}")
+    run_case(env, k, v, slots, n_pg, P, 64, O.ROT_K, what=f"ragged-k H={H} T={T}")
+
+
+def test_strided_views_of_fused_qkv(env):
+    torch, S = env
+    rng = np.random.default_rng(21)
+    T, Hq, H, D = 300, 32, 8, 128
+    qkv = (rng.standard_normal((T, (Hq + 2 * H) * D)) * 2).astype(np.float16)
+    q_end = Hq * D
+    k = qkv[:, q_end:q_end + H * D].reshape(T, H, D)
+    v = qkv[:, q_end + H * D:].reshape(T, H, D)
+    slots = rng.permutation(40 * 16)[:T].astype(np.int64)
+    say("strided qkv")
+    qd = torch.from_numpy(qkv).cuda()
+    kd = qd[:, q_end:q_end + H * D].view(T, H, D)
+    vd = qd[:, q_end + H * D:].view(T, H, D)
+    assert kd.stride(0) == (Hq + 2 * H) * D
+    sd = torch.from_numpy(slots).cuda()
+    gp = gpu_pools(env, 40, 16, H, D)
+    S.quantize_append(kd, vd, sd, *gp, h=128, rot="kv")
+    torch.cuda.synchronize()
+    want = np_pools(40, 16, H, D)
+    O.quantize_append(np.ascontiguousarray(k), np.ascontiguousarray(v), slots, *want, h=128,
+                      rot_mode=O.ROT_KV)
+    assert_pools_equal([to_np(x) for x in gp], want, "strided")
+
+
+def _edge_vectors(rng, T, H):
+    x = (rng.standard_normal((T, H, 128))).astype(np.float32)
+    kinds = []
+    for t in range(T):
+        kind = t % 9
+        kinds.append(kind)
+        if kind == 0:
+            x[t] = 0                                   # zero vector
+        elif kind == 1:
+            x[t] *= 2.0 ** -24 * 3                     # fp16 subnormal inputs
+        elif kind == 2:
+            x[t] = 0
+            x[t, :, 5] = 10 * 2.0 ** -24               # subnormal scale + clamp
+            x[t, :, 6] = -3 * 2.0 ** -24
+        elif kind == 3:
+            x[t] = np.sign(x[t]) * 65504.0             # saturating scale
+        elif kind == 4:
+            x[t] = -65504.0                            # -8 code after saturation
+        elif kind == 5:
+            x[t] = 0
+            x[t, :, 1] = 2.0 ** -24                    # scale underflows to 0
+        elif kind == 6:
+            x[t] *= 1e4
+        elif kind == 7:
+            x[t] = np.round(x[t] * 4) / 4              # exact ties
+    return np.clip(x, -65504, 65504).astype(np.float16)
+
+
+@pytest.mark.parametrize("h,rot", [(128, O.ROT_KV), (32, O.ROT_KV), (128, O.ROT_NONE), (64, O.ROT_K)])
+def test_edge_values(env, h, rot):
+    rng = np.random.default_rng(33)
+    T, H = 200, 4
+    k = _edge_vectors(rng, T, H)
+    v = _edge_vectors(rng, T, H)[::-1].copy()
+    slots = np.arange(T, dtype=np.int64)
+    run_case(env, k, v, slots, 13, 16, h, rot, what=f"edge h={h} rot={rot}")
+
+
+def test_single_tensor_calls(env):
+    rng = np.random.default_rng(44)
+    T, H = 100, 8
+    k = rng.standard_normal((T, H, 128)).astype(np.float16)
+    slots = rng.permutation(7 * 16)[:T].astype(np.int64)
+    run_case(env, k, None, slots, 7, 16, 128, O.ROT_KV, what="k only")
+    run_case(env, None, k, slots, 7, 16, 128, O.ROT_KV, what="v only")
+    run_case(env, None, k, slots, 7, 16, 128, O.ROT_K, what="v only, k-mode (naive v)")
+
+
+def test_naive_entry_points_match_rot_none(env):
+    torch, S = env
+    wl = W.WORKLOADS["sweep"]
+    k, v = W.kv(wl, 0, 0, 512)
+    slots = W.slot_mapping(wl)[:512].copy()
+    say("naive entry points")
+    kd, vd, sd = (torch.from_numpy(a).cuda() for a in (k, v, slots))
+    a = gpu_pools(env, wl.N_pg, wl.P, wl.H, wl.D)
+    b = gpu_pools(env, wl.N_pg, wl.P, wl.H, wl.D)
+    S.naive_int4_append(kd, vd, sd, *a)
+    S.quantize_append(kd, vd, sd, *b, h=128, rot="none")
+    ga = S.naive_int4_gather(*a, sd)
+    gb = S.dequant_gather(*b, sd, rot="none")
+    torch.cuda.synchronize()
+    for x, y in zip(a + ga, b + gb):
+        assert torch.equal(x.view(torch.uint8) if x.dtype == torch.uint8 else x.view(torch.int16),
+                           y.view(torch.uint8) if y.dtype == torch.uint8 else y.view(torch.int16))
+    want = np_pools(wl.N_pg, wl.P, wl.H, wl.D)
+    O.quantize_append(k, v, slots, *want, h=128, rot_mode=O.ROT_NONE)
+    assert_pools_equal([to_np(x) for x in a], want, "naive")
+
+
+def test_zero_tokens_is_a_no_op(env):
+    torch, S = env
+    gp = gpu_pools(env, 2, 16, 8, 128)
+    e = torch.empty((0, 8, 128), dtype=torch.float16, device="cuda")
+    s = torch.empty((0,), dtype=torch.int64, device="cuda")
+    S.quantize_append(e, e, s, *gp)
+    S.dequant_gather(*gp, s)
+    torch.cuda.synchronize()
+    assert bool((gp[0] == SENT_CODE).all())
+
+
+def test_side_stream(env):
+    torch, S = env
+    rng = np.random.default_rng(55)
+    T, H = 256, 8
+    k = rng.standard_normal((T, H, 128)).astype(np.float16)
+    slots = rng.permutation(20 * 16)[:T].astype(np.int64)
+    say("side stream")
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        kd = torch.from_numpy(k).cuda(non_blocking=False)
+        sd = torch.from_numpy(slots).cuda()
+        gp = gpu_pools(env, 20, 16, H, 128)
+        S.quantize_append(kd, kd, sd, *gp, h=128, rot="kv")
+    st.synchronize()
+    want = np_pools(20, 16, H, 128)
+    O.quantize_append(k, k, slots, *want, h=128, rot_mode=O.ROT_KV)
+    assert_pools_equal([to_np(x) for x in gp], want, "side stream")
+
+
+def test_division_route_exhaustive_fp16(env):
+    """Naive path: for 48 scales, every fp16 value y in [-amax, amax] is
+    quantised once (y / s near every half-integer is hit); codes must equal
+    the oracle's rint(f32(y / s)) exactly."""
+    rng = np.random.default_rng(66)
+    all_h = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float32)
+    amaxes = np.concatenate([[7.0, 1.0, 3.5, 65504.0, 2.0 ** -20, 6.0e-5],
+                             np.exp(rng.uniform(np.log(1e-4), np.log(6e4), 42))])
+    rows = []
+    for A in amaxes:
+        A = float(np.float16(A))
+        vals = all_h[all_h <= A]
+        vals = np.concatenate([vals, -vals])
+        vals = vals[rng.permutation(len(vals))]
+        n = -(-len(vals) // 127)
+        block = np.zeros((n, 128), np.float32)
+        block[:, 0] = A
+        flat = np.zeros(n * 127, np.float32)
+        flat[:len(vals)] = vals
+        block[:, 1:] = flat.reshape(n, 127)
+        rows.append(block)
+    x = np.concatenate(rows).astype(np.float16)
+    T = len(x)
+    say(f"division exhaustive: {T} vectors")
+    x = x.reshape(T, 1, 128)
+    slots = np.arange(T, dtype=np.int64)
+    n_pg = -(-T // 16)
+    run_case(env, x, None, slots, n_pg, 16, 128, O.ROT_NONE, gather=True, what="div-naive")
+
+
+# --------------------------------------------------------------------------
+# full-size workloads: sampled tokens + pool-wide properties
+# --------------------------------------------------------------------------
+
+def check_written_rows(env, gp, slots, n_slots, H):
+    """Exactly the mapped rows are written (scales) and no other code byte changed."""
+    torch, S = env
+    ok = (slots >= 0) & (slots < n_slots)
+    want = torch.zeros(n_slots, dtype=torch.bool, device="cuda")
+    want[torch.from_numpy(slots[ok]).cuda()] = True
+    for codes, scales in ((gp[0], gp[2]), (gp[1], gp[3])):
+        s_written = (scales.view(n_slots, H).view(torch.int16) != -1).any(dim=1)
+        assert torch.equal(s_written, want)
+        untouched = codes.view(n_slots, -1)[~want]
+        assert bool((untouched == SENT_CODE).all())
+
+
+def compare_sampled(env, gp, k, v, slots, sample, h, rot, what):
+    """Pool rows of sampled tokens vs the oracle's encoding of those tokens."""
+    torch, S = env
+    H = k.shape[1]
+    idx = torch.from_numpy(slots[sample]).cuda()
+    n_slots = gp[0].shape[0] * gp[0].shape[1]
+    for name, x, codes, scales, rotated in (
+            ("k", k, gp[0], gp[2], rot != O.ROT_NONE), ("v", v, gp[1], gp[3], rot == O.ROT_KV)):
+        got_c = to_np(codes.view(n_slots, H, -1)[idx])
+        got_s = to_np(scales.view(n_slots, H)[idx])
+        want_c, want_s = O.encode_vectors(x[sample], h, rotated)
+        assert got_c.tobytes() == want_c.tobytes(), f"{what} {name} codes"
+        assert got_s.tobytes() == want_s.tobytes(), f"{what} {name} scales"
+
+
+def test_decode_workload_36_layers(env):
+    torch, S = env
+    wl = W.WORKLOADS["decode"]
+    slots = W.slot_mapping(wl)
+    sd = torch.from_numpy(slots).cuda()
+    say("decode: 36 layers")
+    for layer in range(wl.layers):
+        k, v = W.kv(wl, layer)
+        gp = gpu_pools(env, wl.N_pg, wl.P, wl.H, wl.D)
+        S.quantize_append(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), sd, *gp,
+                          h=wl.h, rot=ROTS[wl.rot_mode])
+        torch.cuda.synchronize()
+        compare_sampled(env, gp, k, v, slots, np.arange(wl.T), wl.h, wl.rot_mode,
+                        f"decode layer {layer}")
+        if layer in (0, wl.layers - 1):
+            check_written_rows(env, gp, slots, wl.n_slots, wl.H)
+        del gp
+
+
+def _full(env, name, h=None, rot=None, n_sample=4096, gather=False):
+    torch, S = env
+    wl = W.WORKLOADS[name]
+    h = wl.h if h is None else h
+    rot = wl.rot_mode if rot is None else rot
+    say(f"{name}: generating {wl.T} tokens")
+    k, v = W.kv(wl)
+    slots = W.slot_mapping(wl)
+    kd, vd, sd = (torch.from_numpy(a).cuda() for a in (k, v, slots))
+    gp = gpu_pools(env, wl.N_pg, wl.P, wl.H, wl.D)
+    say(f"{name}: append h={h} rot={ROTS[rot]}")
+    S.quantize_append(kd, vd, sd, *gp, h=h, rot=ROTS[rot])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(wl.wid * 7 + h + rot)
+    sample = np.sort(rng.choice(wl.T, size=min(n_sample, wl.T), replace=False))
+    sample[0], sample[-1] = 0, wl.T - 1
+    compare_sampled(env, gp, k, v, slots, sample, h, rot, f"{name} h={h} rot={rot}")
+    check_written_rows(env, gp, slots, wl.n_slots, wl.H)
+    if gather:
+        say(f"{name}: gather")
+        ko, vo = S.dequant_gather(*gp, sd, h=h, rot=ROTS[rot])
+        torch.cuda.synchronize()
+        for x, out, rotated in ((k, ko, rot != O.ROT_NONE), (v, vo, rot == O.ROT_KV)):
+            want = O.decode_vectors(*O.encode_vectors(x[sample], h, rotated), h, rotated)
+            got = to_np(out[torch.from_numpy(sample).cuda()])
+            assert_rows_close(got, want, f"{name} gather")
+    return wl
+
+
+def test_prefill_workload(env):
+    _full(env, "prefill", gather=True)
+
+
+@pytest.mark.parametrize("h,rot", W.SWEEP_VARIANTS)
+def test_sweep_workload(env, h, rot):
+    _full(env, "sweep", h=h, rot=rot, n_sample=2048, gather=True)
+
+
+def test_long_workload_round_trip(env):
+    wl = _full(env, "long", n_sample=2048, gather=True)
+    assert wl.T == wl.n_slots          # exact-fit pool: every slot written
