@@ -1,0 +1,234 @@
+"""Benchmark of the fused Hadamard + INT4 paged append (sawkv) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
+
+One step = one sawkv_quantize_append call over the workload's batch (rotate,
+token-wise INT4, pack, scatter into the paged pool: the whole write path).
+Inputs are generated, uploaded and resident in HBM before timing starts.
+Prints ONE JSON line. Alongside the step it times, on the same batch:
+  * the naive-INT4 control (sawkv_naive_int4_append), interleaved with the
+    rotated kernel, for the rotate-vs-naive ratio;
+  * the read-back (sawkv_dequant_gather) of the same slots;
+  * the CPU oracle on a bounded sample of the same batch (a baseline only).
+Roofline: achieved HBM GB/s of the append kernel (algorithmic bytes per launch
+over the event-timed average launch) against the MI355X HBM3E peak, 8 TB/s.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from int4_kv_cache_amd import workloads as W  # noqa: E402
+
+METRIC = ("GB/s and tokens/s of fused Hadamard+INT4 paged append; % HBM peak; "
+          "vs naive INT4")
+HBM_PEAK_GBPS = 8000.0
+ROT_NAME = {0: "none", 1: "k", 2: "kv"}
+KERNEL_SRC = [os.path.join(ROOT, "int4_kv_cache_amd", "csrc", f)
+              for f in ("sawkv.hip", "sawkv_device.hpp")]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SRC:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload)
+    if not ent or ent.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def describe(wl, h, rot):
+    vals = {"normal": "N(0,1)", "student_t4": "Student-t(4)"}[wl.values]
+    return (f"{wl.name}: {wl.n_seq} seq x {wl.seq_len} tok, {wl.H} KV heads x {wl.D}, "
+            f"{vals} + outliers {wl.outliers}, h={h}, rot={ROT_NAME[rot]}, page {wl.P}, "
+            f"{wl.placement} slots, {wl.layers} layer(s)")
+
+
+def cpu_baseline(wl, h, rot, sample_tokens):
+    """The oracle, untuned, on the first `sample_tokens` tokens of the batch
+    (encode K and V and scatter into host pools)."""
+    from oracle import sawint4 as O
+    k, v = W.kv(wl, 0, 0, sample_tokens)
+    slots = W.slot_mapping(wl)[:sample_tokens]
+    kc = np.zeros((wl.N_pg, wl.P, wl.H, wl.D // 2), np.uint8)
+    vc = np.zeros_like(kc)
+    ks = np.zeros((wl.N_pg, wl.P, wl.H), np.float16)
+    vs = np.zeros_like(ks)
+    t0 = time.perf_counter()
+    O.quantize_append(k, v, slots, kc, vc, ks, vs, h=h, rot_mode=rot)
+    dt = time.perf_counter() - t0
+    gbps = sample_tokens * wl.bytes_per_token() / dt / 1e9
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "tokens_per_s": round(sample_tokens / dt, 1), "seconds": round(dt, 2),
+            "sample": f"first {sample_tokens} tokens of the {wl.name} batch (K and V), "
+                      f"numpy float32 oracle, single thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill", choices=["prefill", "decode", "sweep", "long"])
+    ap.add_argument("--h", type=int, default=None)
+    ap.add_argument("--rot", default=None, choices=["none", "k", "kv"])
+    ap.add_argument("--cpu-sample", type=int, default=32768)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the append/gather path has no exchange "
+              "step, so a multi-GPU figure is not produced (run with --gpus 1).",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    from int4_kv_cache_amd import sawkv as S
+
+    wl = W.WORKLOADS[args.workload]
+    h = args.h or wl.h
+    rot = {"none": 0, "k": 1, "kv": 2}[args.rot] if args.rot else wl.rot_mode
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layers = wl.layers
+
+    print(f"[bench] generating {describe(wl, h, rot)}", file=sys.stderr, flush=True)
+    slots = torch.from_numpy(W.slot_mapping(wl)).to(dev)
+    kvs = []
+    for layer in range(layers):
+        k, v = W.kv(wl, layer)
+        kvs.append((torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)))
+        del k, v
+    pools = [S.alloc_pools(wl.N_pg, wl.P, wl.H, wl.D, dev) for _ in range(layers)]
+    naive_pools = pools   # the control writes the same bytes to the same rows
+    stream = torch.cuda.current_stream()
+
+    def step_rot():
+        for layer in range(layers):
+            S.quantize_append(kvs[layer][0], kvs[layer][1], slots, *pools[layer], h=h,
+                              rot=ROT_NAME[rot], stream=stream)
+
+    def step_naive():
+        for layer in range(layers):
+            S.naive_int4_append(kvs[layer][0], kvs[layer][1], slots, *naive_pools[layer],
+                                stream=stream)
+
+    def step_gather(outs):
+        for layer in range(layers):
+            S.dequant_gather(*pools[layer], slots, h=h, rot=ROT_NAME[rot],
+                             k_out=outs[layer][0], v_out=outs[layer][1], stream=stream)
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n      # ms per step
+
+    # warm-up, then the timed K steps (wall clock bracketed by synchronize)
+    for _ in range(args.warmup):
+        step_rot()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step_rot()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    event_ms = e0.elapsed_time(e1) / args.steps
+
+    tokens = wl.T * layers
+    bytes_step = wl.T * wl.bytes_per_token() * layers
+    gbps = bytes_step / (wall_ms * 1e-3) / 1e9
+    achieved = bytes_step / (event_ms * 1e-3) / 1e9
+
+    # rotated vs naive: interleaved rounds on the same inputs and pools
+    rounds = 7
+    n_ab = max(5, args.steps // 5)
+    rot_ms, naive_ms = [], []
+    for _ in range(rounds):
+        naive_ms.append(timed(step_naive, n_ab))
+        rot_ms.append(timed(step_rot, n_ab))
+    ratio = float(np.median(rot_ms) / np.median(naive_ms))
+
+    # read-back of the same slots
+    outs = [(torch.empty_like(kvs[l][0]), torch.empty_like(kvs[l][1])) for l in range(layers)]
+    for _ in range(3):
+        step_gather(outs)
+    g_ms = timed(lambda: step_gather(outs), max(5, args.steps // 2))
+
+    traffic = measured_traffic(args.workload)
+    out = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": describe(wl, h, rot), "tokens_per_step": tokens,
+                   "heads": wl.H, "head_dim": wl.D, "block_size_h": h,
+                   "rotation": ROT_NAME[rot], "page_size": wl.P, "pages": wl.N_pg,
+                   "layers_per_step": layers, "parallelism": "single GPU"},
+        "step": "sawkv_quantize_append over the batch (rotate, token-wise INT4, pack, "
+                "paged scatter), one call per layer",
+        "tokens_per_s": round(tokens / (wall_ms * 1e-3), 1),
+        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": wl.T * wl.bytes_per_token(),
+                     "kernel": "sawkv::append_kernel"},
+        "vs_naive": {"rot_ms_median": round(float(np.median(rot_ms)), 5),
+                     "naive_ms_median": round(float(np.median(naive_ms)), 5),
+                     "rot_over_naive": round(ratio, 4),
+                     "naive_GBps": round(bytes_step / (np.median(naive_ms) * 1e-3) / 1e9, 2),
+                     "rounds": rounds, "steps_per_round": n_ab},
+        "gather": {"ms_per_step": round(g_ms, 5),
+                   "GBps": round(bytes_step / (g_ms * 1e-3) / 1e9, 2),
+                   "tokens_per_s": round(tokens / (g_ms * 1e-3), 1)},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu:
+        n = min(args.cpu_sample, wl.T)
+        print(f"[bench] cpu baseline: oracle on {n} tokens", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, h, rot, n)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

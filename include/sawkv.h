@@ -40,6 +40,8 @@
  *     text from sawkv_last_error().
  *   - A slot < 0 or >= N_pg*P is skipped by append and yields a zero row in
  *     gather (no byte outside the addressed rows is ever touched).
+ *   - T == 0 returns SAWKV_OK after the size checks, launches nothing and
+ *     reads no pointer (NULL tensors are accepted then).
  *   - Caller preconditions not checked: no two tokens of one call share a
  *     slot (which write wins is then unspecified); inputs, outputs and pools
  *     do not overlap; K/V values are finite.

@@ -208,7 +208,7 @@ __device__ __forceinline__ void gather_one(const GatherTensor& G, const GatherPa
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      x[8 * i + j] = (float)__builtin_amdgcn_sbfe((int)d[i], 4 * j, 4);
+      x[8 * i + j] = (float)(int)__builtin_amdgcn_sbfe(d[i], 4 * j, 4);   // signed nibble
 
   float o[kElems];
   if constexpr (HB == 0) {
@@ -219,9 +219,12 @@ __device__ __forceinline__ void gather_one(const GatherTensor& G, const GatherPa
     const float sgn = fwht_rest<HB>(x, lam);
     const float csg = c_h<HB>() * sgn;
     // (F q) * s is exact; one rounding for * c_h; the + 0 turns a -0 that the
-    // sign bookkeeping may leave on an exact zero into +0
+    // sign bookkeeping may leave on an exact zero into +0. The float32 result
+    // is pinned (opaque) so that the fp16 conversion below rounds it a second
+    // time, as defined: otherwise the compiler may fuse fma + convert into one
+    // v_fma_mixlo_f16, which rounds once and differs at f16 midpoints.
 #pragma unroll
-    for (int k = 0; k < kElems; ++k) o[k] = __builtin_fmaf(x[k] * sf, csg, 0.0f);
+    for (int k = 0; k < kElems; ++k) o[k] = opaque(__builtin_fmaf(x[k] * sf, csg, 0.0f));
   }
 
   if (in_range) {
@@ -285,7 +288,7 @@ int check_geometry(int64_t T, int32_t H, int32_t D, int64_t N_pg, int32_t P, int
     return fail(SAWKV_EINVAL, "rot_mode = %d invalid", rot_mode);
   if (T * (int64_t)H >= (INT64_C(1) << 31))
     return fail(SAWKV_EUNSUPPORTED, "T*H = %lld too large (< 2^31)", (long long)(T * H));
-  if (slots == nullptr) return fail(SAWKV_EINVAL, "slot_mapping is NULL");
+  if (slots == nullptr && T > 0) return fail(SAWKV_EINVAL, "slot_mapping is NULL");
   if (!aligned(slots, 8)) return fail(SAWKV_EALIGN, "slot_mapping not 8-byte aligned");
   return SAWKV_OK;
 }
@@ -342,10 +345,10 @@ int append_impl(const void* k, const void* v, int64_t k_stride, int64_t v_stride
                 int32_t h, int32_t rot_mode, void* stream) {
   int st = check_geometry(T, H, D, N_pg, P, h, rot_mode, slots);
   if (st) return st;
+  if (T == 0) return ok();              // nothing is read or written
   if (k == nullptr && v == nullptr) return fail(SAWKV_EINVAL, "both k and v are NULL");
   if (k && (st = check_tensor("k", k, k_stride, k_codes, k_scales, H, D))) return st;
   if (v && (st = check_tensor("v", v, v_stride, v_codes, v_scales, H, D))) return st;
-  if (T == 0) return ok();
 
   sawkv::AppendParams p{};
   int n = 0, hb[2] = {0, 0};
@@ -372,10 +375,10 @@ int gather_impl(const void* k_codes, const void* v_codes, const void* k_scales,
                 int32_t rot_mode, void* stream) {
   int st = check_geometry(T, H, D, N_pg, P, h, rot_mode, slots);
   if (st) return st;
+  if (T == 0) return ok();
   if (k_out == nullptr && v_out == nullptr) return fail(SAWKV_EINVAL, "both outputs are NULL");
   if (k_out && (st = check_tensor("k", k_out, -1, k_codes, k_scales, H, D))) return st;
   if (v_out && (st = check_tensor("v", v_out, -1, v_codes, v_scales, H, D))) return st;
-  if (T == 0) return ok();
 
   sawkv::GatherParams p{};
   int n = 0, hb[2] = {0, 0};

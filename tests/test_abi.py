@@ -96,6 +96,7 @@ def gat(lib, **kw):
     (dict(T=1 << 31, H=1), EUNSUPPORTED),
     (dict(slots=None), EINVAL),
     (dict(slots=S + 4), EALIGN),
+    (dict(slots=S + 4, T=0), EALIGN),
     (dict(k=None, v=None), EINVAL),
     (dict(kc=None), EINVAL),
     (dict(vss=None), EINVAL),
@@ -132,7 +133,10 @@ def test_naive_entry_points_validate(lib):
 
 def test_zero_tokens_launch_nothing(lib):
     assert app(lib, T=0) == OK
+    assert app(lib, T=0, k=None, v=None, slots=None) == OK      # empty tensors: NULL data
+    assert gat(lib, T=0, ko=None, vo=None, slots=None) == OK
     assert lib.sawkv_last_error() == b""
+    assert app(lib, T=0, D=64) == EUNSUPPORTED                   # sizes still checked
     assert gat(lib, T=0) == OK
     assert app(lib, T=0, v=None, vc=None, vss=None, rot=1) == OK
     assert lib.sawkv_naive_int4_append(K, None, 1024, 0, S, 0, 8, 128, KC, None, KS, None, 4,

@@ -68,15 +68,23 @@ def assert_pools_equal(got, want, what=""):
 
 
 def assert_rows_close(got, want, what=""):
-    """fp16 [N, H, D]: byte-identical, and per vector within 1e-3 of its max."""
+    """fp16 [N, H, D]: per vector within 1e-3 of its largest finite magnitude
+    (non-finite reference values - fp16 overflow of q * s on read-back of a
+    saturated scale - must be matched exactly), and byte-identical overall."""
     g = np.asarray(got).astype(np.float64)
     w = np.asarray(want).astype(np.float64)
-    scale = np.max(np.abs(w), axis=-1, keepdims=True)
-    err = np.max(np.abs(g - w), axis=-1, keepdims=True)
+    fin = np.isfinite(w)
+    assert np.array_equal(g[~fin], w[~fin]), f"{what}: non-finite values differ"
+    wf = np.where(fin, w, 0.0)
+    gf = np.where(fin, g, 0.0)
+    scale = np.max(np.abs(wf), axis=-1, keepdims=True)
+    err = np.max(np.abs(gf - wf), axis=-1, keepdims=True)
     assert np.all(err <= 1e-3 * scale), f"{what}: tolerance exceeded, max {np.max(err / np.maximum(scale, 1e-30))}"
     gb, wb = np.asarray(got).view(np.uint16), np.asarray(want).view(np.uint16)
-    nbad = int(np.sum(gb != wb))
-    assert nbad == 0, f"{what}: {nbad} fp16 values differ in bits"
+    bad = np.argwhere(gb != wb)
+    detail = [(tuple(int(i) for i in b), hex(int(gb[tuple(b)])), hex(int(wb[tuple(b)])))
+              for b in bad[:6]]
+    assert len(bad) == 0, f"{what}: {len(bad)} fp16 values differ in bits: {detail}"
 
 
 def run_case(env, k, v, slots, n_pg, P, h, rot, gather=True, what=""):
