@@ -88,12 +88,12 @@ def cpu_baseline(wl, h, rot, sample_tokens):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="prefill", choices=["prefill", "decode", "sweep", "long"])
     ap.add_argument("--h", type=int, default=None)
     ap.add_argument("--rot", default=None, choices=["none", "k", "kv"])
-    ap.add_argument("--cpu-sample", type=int, default=32768)
+    ap.add_argument("--cpu-sample", type=int, default=131072)
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
 
@@ -171,7 +171,7 @@ def main():
 
     # rotated vs naive: interleaved rounds on the same inputs and pools
     rounds = 7
-    n_ab = max(5, args.steps // 5)
+    n_ab = max(20, args.steps // 4)
     rot_ms, naive_ms = [], []
     for _ in range(rounds):
         naive_ms.append(timed(step_naive, n_ab))
@@ -182,7 +182,15 @@ def main():
     outs = [(torch.empty_like(kvs[l][0]), torch.empty_like(kvs[l][1])) for l in range(layers)]
     for _ in range(3):
         step_gather(outs)
-    g_ms = timed(lambda: step_gather(outs), max(5, args.steps // 2))
+    g_ms = timed(lambda: step_gather(outs), max(20, args.steps // 2))
+
+    # attainable-bandwidth context on this machine: a 256 MiB device copy (torch)
+    cbuf = torch.empty(64 * 1024 * 1024, dtype=torch.int32, device=dev)
+    cdst = torch.empty_like(cbuf)
+    cdst.copy_(cbuf)
+    c_ms = timed(lambda: cdst.copy_(cbuf), 50)
+    copy_gbps = 2 * cbuf.numel() * 4 / (c_ms * 1e-3) / 1e9
+    del cbuf, cdst
 
     traffic = measured_traffic(args.workload)
     out = {
@@ -219,6 +227,8 @@ def main():
         "gather": {"ms_per_step": round(g_ms, 5),
                    "GBps": round(bytes_step / (g_ms * 1e-3) / 1e9, 2),
                    "tokens_per_s": round(tokens / (g_ms * 1e-3), 1)},
+        "attainable": {"copy_256MiB_GBps": round(copy_gbps, 1),
+                       "note": "torch device-to-device copy on the same GPU, context only"},
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu:

@@ -40,8 +40,10 @@ struct AppendParams {
   AppendTensor t[2];     // blockIdx.y selects the tensor
   const int64_t* slots;  // [T]
   int64_t n_slots;       // N_pg * P
+  int32_t T;
   int32_t TH;            // T * H vectors per tensor
   int32_t H;
+  uint32_t h_magic;      // ceil(2^20 / H): n / H = (n * h_magic) >> 20 for n < 2^9
 };
 
 // y = float32 input, or f32(c_h * F_h(x)) with the lane's sign removed.
@@ -82,25 +84,53 @@ __device__ __forceinline__ void load_transform(const uint4 (&raw)[4], float (&y)
   }
 }
 
-template <int HB>
-__device__ __forceinline__ void append_one(const AppendTensor& A, const AppendParams& p) {
-  const int lane = threadIdx.x & 63;
-  const int lam = lane & 3;
-  int v = (blockIdx.x * kWaves + (threadIdx.x >> 6)) * kVecPerWave + (lane >> 2);
-  const bool in_range = v < p.TH;
-  if (!in_range) v = p.TH - 1;            // compute on a valid vector, store nothing
-  const int t = (int)((uint32_t)v / (uint32_t)p.H);
-  const int head = v - t * p.H;
-  const int64_t slot = p.slots[t];
-  const bool store = in_range && slot >= 0 && slot < p.n_slots;
+// (a << 4) | b as one instruction (kept from being re-associated)
+__device__ __forceinline__ uint32_t shl4_or(uint32_t a, uint32_t b) {
+  uint32_t d;
+  asm("v_lshl_or_b32 %0, %1, 4, %2" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ uint32_t shl8_or(uint32_t a, uint32_t b) {
+  uint32_t d;
+  asm("v_lshl_or_b32 %0, %1, 8, %2" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
 
-  const __half* src = A.src + (int64_t)t * A.stride + head * kD + 8 * lam;
+// One wave's share of work: 16 consecutive (token, head) vectors, loaded.
+struct Fetched {
   uint4 raw[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) raw[i] = *reinterpret_cast<const uint4*>(src + 32 * i);
+  int64_t slot;
+  int32_t head;
+  bool in_range;
+};
 
+// Wave-uniform position of the first vector of a batch: v0 = t0 * H + h0.
+struct WavePos {
+  uint32_t v0, t0, h0;
+};
+
+__device__ __forceinline__ Fetched fetch_batch(const AppendTensor& A, const AppendParams& p,
+                                               WavePos w, int lam, int vq) {
+  Fetched f;
+  const uint32_t n = w.h0 + (uint32_t)vq;                 // < H + 16
+  uint32_t dt = (n * p.h_magic) >> 20;                    // n / H, exact for n < 2^9
+  f.head = (int32_t)(n - dt * (uint32_t)p.H);
+  f.in_range = w.v0 + (uint32_t)vq < (uint32_t)p.TH;
+  dt = min(dt, (uint32_t)p.T - 1u - w.t0);                // out-of-range lanes: a valid row
+  const char* base = reinterpret_cast<const char*>(A.src) + (int64_t)w.t0 * A.stride * 2;
+  const uint32_t off = dt * (uint32_t)A.stride * 2u + (uint32_t)f.head * (kD * 2) + 16u * lam;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    f.raw[i] = *reinterpret_cast<const uint4*>(base + off + 64 * i);
+  f.slot = p.slots[w.t0 + dt];
+  return f;
+}
+
+template <int HB>
+__device__ __forceinline__ void quantize_store(const AppendTensor& A, const AppendParams& p,
+                                               const Fetched& f, int lam) {
   float y[kElems];
-  load_transform<HB>(raw, y, lam);
+  load_transform<HB>(f.raw, y, lam);
 
   // token-wise scale: amax over the 128 channels of the vector (4 lanes)
   float m = 0.0f;
@@ -131,23 +161,23 @@ __device__ __forceinline__ void append_one(const AppendTensor& A, const AppendPa
     for (int k = 0; k < kElems; ++k) u[k] = min(max(u[k], 0x4B400000u), 0x4B40000Fu);
   }
 
-  // pack: byte b of chunk i = (q_{2b} & 15) | (q_{2b+1} & 15) << 4; nibbles
-  // hold q + 8 until the final xor with 0x8 per nibble
+  // pack: byte b of chunk i = (q_{2b} & 15) | (q_{2b+1} & 15) << 4; the
+  // nibbles hold q + 8 until the final xor with 0x8 per nibble
   uint32_t d[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t* w = u + 8 * i;
-    const uint32_t p01 = (w[1] << 4) | w[0];    // byte 0 valid, byte 1 zero
-    const uint32_t p23 = (w[3] << 4) | w[2];
-    const uint32_t p45 = (w[5] << 4) | w[4];
-    const uint32_t p67 = (w[7] << 4) | w[6];
-    const uint32_t lo = (p23 << 8) | p01;       // bytes 0-1 valid
-    const uint32_t hi = (p67 << 8) | p45;
+    const uint32_t p01 = shl4_or(w[1], w[0]);   // byte 0 = nibbles 0,1; byte 1 = 0
+    const uint32_t p23 = shl4_or(w[3], w[2]);
+    const uint32_t p45 = shl4_or(w[5], w[4]);
+    const uint32_t p67 = shl4_or(w[7], w[6]);
+    const uint32_t lo = shl8_or(p23, p01);      // bytes 0-1 valid
+    const uint32_t hi = shl8_or(p67, p45);
     d[i] = __builtin_amdgcn_perm(hi, lo, 0x05040100u) ^ 0x88888888u;
   }
 
-  if (store) {
-    const int64_t row = slot * p.H + head;
+  if (f.in_range && f.slot >= 0 && f.slot < p.n_slots) {
+    const int64_t row = f.slot * p.H + f.head;
     uint8_t* dst = A.codes + row * (kD / 2) + 4 * lam;
 #pragma unroll
     for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(dst + 16 * i) = d[i];
@@ -155,10 +185,28 @@ __device__ __forceinline__ void append_one(const AppendTensor& A, const AppendPa
   }
 }
 
+// One wave: 16 consecutive (token, head) vectors of one tensor. (A persistent
+// loop with next-batch prefetch measured slower on MI355X than this one-shot
+// grid: the kernel is bound by HBM, and the one-shot grid keeps more waves
+// resident.)
+template <int HB>
+__device__ __forceinline__ void append_tensor(const AppendTensor& A, const AppendParams& p) {
+  const int lane = threadIdx.x & 63;
+  const int lam = lane & 3;
+  const int vq = lane >> 2;
+  const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  WavePos w;
+  w.v0 = (blockIdx.x * kWaves + wave) * kVecPerWave;      // wave-uniform
+  if (w.v0 >= (uint32_t)p.TH) return;
+  w.t0 = w.v0 / (uint32_t)p.H;
+  w.h0 = w.v0 - w.t0 * (uint32_t)p.H;
+  quantize_store<HB>(A, p, fetch_batch(A, p, w, lam, vq), lam);
+}
+
 template <int HB0, int HB1>
 __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p) {
-  if (blockIdx.y == 0) append_one<HB0>(p.t[0], p);
-  else append_one<HB1>(p.t[1], p);
+  if (blockIdx.y == 0) append_tensor<HB0>(p.t[0], p);
+  else append_tensor<HB1>(p.t[1], p);
 }
 
 // ---------------------------------------------------------------------------
@@ -175,76 +223,191 @@ struct GatherParams {
   GatherTensor t[2];
   const int64_t* slots;
   int64_t n_slots;
+  int32_t T;
   int32_t TH;
   int32_t H;
+  uint32_t h_magic;      // ceil(2^20 / H)
 };
 
-template <int HB>
-__device__ __forceinline__ void gather_one(const GatherTensor& G, const GatherParams& p) {
-  const int lane = threadIdx.x & 63;
-  const int lam = lane & 3;
-  int v = (blockIdx.x * kWaves + (threadIdx.x >> 6)) * kVecPerWave + (lane >> 2);
-  const bool in_range = v < p.TH;
-  if (!in_range) v = p.TH - 1;
-  const int t = (int)((uint32_t)v / (uint32_t)p.H);
-  const int head = v - t * p.H;
-  const int64_t slot = p.slots[t];
-  const bool valid = slot >= 0 && slot < p.n_slots;
+struct GatherFetched {
+  uint32_t d[4];         // this lane's 32 codes (4 chunks of 8 nibbles)
+  float sf;              // scale of the vector (0 for an invalid slot)
+  int32_t v;             // vector index t * H + head (clamped into range)
+  int32_t v0;            // first vector of the wave's batch
+  int32_t TH;
+  bool in_range;
+};
 
-  uint32_t d[4] = {0u, 0u, 0u, 0u};
-  float sf = 0.0f;
-  if (valid) {
+__device__ __forceinline__ GatherFetched gather_fetch(const GatherTensor& G,
+                                                      const GatherParams& p, uint32_t v0,
+                                                      int lam, int vq) {
+  GatherFetched f;
+  const uint32_t H = (uint32_t)p.H;
+  const uint32_t t0 = v0 / H, h0 = v0 - t0 * H;           // wave-uniform
+  const uint32_t n = h0 + (uint32_t)vq;
+  uint32_t dt = (n * p.h_magic) >> 20;                    // n / H, exact for n < 2^9
+  const uint32_t head = n - dt * H;
+  f.in_range = v0 + (uint32_t)vq < (uint32_t)p.TH;
+  dt = min(dt, (uint32_t)p.T - 1u - t0);
+  f.v = (int32_t)((t0 + dt) * H + head);
+  f.v0 = (int32_t)v0;
+  f.TH = p.TH;
+  const int64_t slot = p.slots[t0 + dt];
+  f.d[0] = f.d[1] = f.d[2] = f.d[3] = 0u;
+  f.sf = 0.0f;
+  if (slot >= 0 && slot < p.n_slots) {
     const int64_t row = slot * p.H + head;
     const uint8_t* src = G.codes + row * (kD / 2) + 4 * lam;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) d[i] = *reinterpret_cast<const uint32_t*>(src + 16 * i);
-    sf = __half2float(G.scales[row]);
+    for (int i = 0; i < 4; ++i) f.d[i] = *reinterpret_cast<const uint32_t*>(src + 16 * i);
+    f.sf = __half2float(G.scales[row]);
   }
+  return f;
+}
 
-  // integer codes; every butterfly partial sum is an integer of magnitude
-  // <= 1024, so the transform is exact in float32 and its order is immaterial
-  float x[kElems];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      x[8 * i + j] = (float)(int)__builtin_amdgcn_sbfe(d[i], 4 * j, 4);   // signed nibble
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 
+__device__ __forceinline__ h2v h2_of(uint32_t u) { return __builtin_bit_cast(h2v, u); }
+__device__ __forceinline__ uint32_t u_of(h2v v) { return __builtin_bit_cast(uint32_t, v); }
+
+template <int HB>
+__device__ __forceinline__ void gather_compute_store(const GatherTensor& G,
+                                                     const GatherFetched& f, int lam) {
   float o[kElems];
   if constexpr (HB == 0) {
+    float x[kElems];
 #pragma unroll
-    for (int k = 0; k < kElems; ++k) o[k] = x[k] * sf;     // exact
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        x[8 * i + j] = (float)(int)__builtin_amdgcn_sbfe(f.d[i], 4 * j, 4);
+#pragma unroll
+    for (int k = 0; k < kElems; ++k) o[k] = x[k] * f.sf;     // exact
   } else {
-    lane_stage<0>(x);
-    const float sgn = fwht_rest<HB>(x, lam);
-    const float csg = c_h<HB>() * sgn;
-    // (F q) * s is exact; one rounding for * c_h; the + 0 turns a -0 that the
-    // sign bookkeeping may leave on an exact zero into +0. The float32 result
-    // is pinned (opaque) so that the fp16 conversion below rounds it a second
-    // time, as defined: otherwise the compiler may fuse fma + convert into one
-    // v_fma_mixlo_f16, which rounds once and differs at f16 midpoints.
-#pragma unroll
-    for (int k = 0; k < kElems; ++k) o[k] = opaque(__builtin_fmaf(x[k] * sf, csg, 0.0f));
-  }
-
-  if (in_range) {
-    __half* dst = G.out + (int64_t)v * kD + 8 * lam;
+    // codes as fp16 pairs P[i][m] = (channel 8i+m, channel 8i+m+4); every
+    // partial sum is an integer of magnitude <= 1024, exact in fp16
+    h2v P[4][4];
+    const h2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint4 w;
-      w.x = __builtin_bit_cast(uint32_t, __floats2half2_rn(o[8 * i + 0], o[8 * i + 1]));
-      w.y = __builtin_bit_cast(uint32_t, __floats2half2_rn(o[8 * i + 2], o[8 * i + 3]));
-      w.z = __builtin_bit_cast(uint32_t, __floats2half2_rn(o[8 * i + 4], o[8 * i + 5]));
-      w.w = __builtin_bit_cast(uint32_t, __floats2half2_rn(o[8 * i + 6], o[8 * i + 7]));
-      *reinterpret_cast<uint4*>(dst + 32 * i) = w;
+      const uint32_t x = f.d[i] ^ 0x88888888u;              // nibble + 8 in 0..15
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        P[i][m] = h2_of(((x >> (4 * m)) & 0x000F000Fu) | 0x64006400u) - off;   // 1024+n-1032
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int m = 0; m < 4; m += 2) {                       // stride 1
+        const h2v a = P[i][m], b = P[i][m + 1];
+        P[i][m] = a + b; P[i][m + 1] = a - b;
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {                          // stride 2
+        const h2v a = P[i][m], b = P[i][m + 2];
+        P[i][m] = a + b; P[i][m + 2] = a - b;
+      }
+      const h2v pm = {(_Float16)1.0f, (_Float16)-1.0f};
+#pragma unroll
+      for (int m = 0; m < 4; ++m)                            // stride 4 (lo, hi)
+        P[i][m] = __builtin_elementwise_fma(P[i][m].yy, pm, P[i][m].xx);
+    }
+    float sgn = 1.0f;
+    if constexpr (HB > 8) {                                  // stride 8
+      const float sg = (lam & 1) ? -1.0f : 1.0f;
+      const h2v s2 = {(_Float16)sg, (_Float16)sg};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          P[i][m] = __builtin_elementwise_fma(
+              h2_of((uint32_t)__builtin_amdgcn_mov_dpp((int)u_of(P[i][m]), 0xB1, 0xF, 0xF, true)),
+              s2, P[i][m]);
+      sgn *= sg;
+    }
+    if constexpr (HB > 16) {                                 // stride 16
+      const float sg = (lam & 2) ? -1.0f : 1.0f;
+      const h2v s2 = {(_Float16)sg, (_Float16)sg};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          P[i][m] = __builtin_elementwise_fma(
+              h2_of((uint32_t)__builtin_amdgcn_mov_dpp((int)u_of(P[i][m]), 0x4E, 0xF, 0xF, true)),
+              s2, P[i][m]);
+      sgn *= sg;
+    }
+    if constexpr (HB > 32) {                                 // stride 32
+#pragma unroll
+      for (int i = 0; i < 4; i += 2)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const h2v a = P[i][m], b = P[i + 1][m];
+          P[i][m] = a + b; P[i + 1][m] = a - b;
+        }
+    }
+    if constexpr (HB > 64) {                                 // stride 64
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const h2v a = P[i][m], b = P[i + 2][m];
+          P[i][m] = a + b; P[i + 2][m] = a - b;
+        }
+    }
+    const float csg = c_h<HB>() * sgn;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float t_lo = __builtin_fmaf((float)P[i][m].x, f.sf, 0.0f);   // exact
+        const float t_hi = __builtin_fmaf((float)P[i][m].y, f.sf, 0.0f);
+        o[8 * i + m] = opaque(__builtin_fmaf(t_lo, csg, 0.0f));
+        o[8 * i + m + 4] = opaque(__builtin_fmaf(t_hi, csg, 0.0f));
+      }
   }
+
+  // stage the wave's 16 output rows (4 KB) through LDS, then store them as
+  // four fully contiguous 1 KB wave stores; rows padded to 272 bytes
+  __shared__ uint4 stage[kWaves][kVecPerWave][17];
+  const int wv = threadIdx.x >> 6, vq = (threadIdx.x & 63) >> 2;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint4 w;
+    w.x = __builtin_bit_cast(uint32_t, __floats2half2_rn(o[8 * i + 0], o[8 * i + 1]));
+    w.y = __builtin_bit_cast(uint32_t, __floats2half2_rn(o[8 * i + 2], o[8 * i + 3]));
+    w.z = __builtin_bit_cast(uint32_t, __floats2half2_rn(o[8 * i + 4], o[8 * i + 5]));
+    w.w = __builtin_bit_cast(uint32_t, __floats2half2_rn(o[8 * i + 6], o[8 * i + 7]));
+    stage[wv][vq][4 * i + lam] = w;
+  }
+  __builtin_amdgcn_wave_barrier();
+  const int lane = threadIdx.x & 63;
+  const int32_t v_first = f.v0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * i + (lane >> 4), c = lane & 15;
+    const uint4 w = stage[wv][r][c];
+    if (v_first + r < f.TH)
+      *reinterpret_cast<uint4*>(G.out + ((int64_t)v_first + r) * kD + 8 * c) = w;
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int HB>
+__device__ __forceinline__ void gather_tensor(const GatherTensor& G, const GatherParams& p) {
+  const int lane = threadIdx.x & 63;
+  const int lam = lane & 3;
+  const int vq = lane >> 2;
+  const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t v0 = (blockIdx.x * kWaves + wave) * kVecPerWave;
+  if (v0 >= (uint32_t)p.TH) return;
+  gather_compute_store<HB>(G, gather_fetch(G, p, v0, lam, vq), lam);
 }
 
 template <int HB0, int HB1>
 __global__ __launch_bounds__(kThreads) void gather_kernel(GatherParams p) {
-  if (blockIdx.y == 0) gather_one<HB0>(p.t[0], p);
-  else gather_one<HB1>(p.t[1], p);
+  if (blockIdx.y == 0) gather_tensor<HB0>(p.t[0], p);
+  else gather_tensor<HB1>(p.t[1], p);
 }
 
 }  // namespace sawkv
@@ -286,6 +449,7 @@ int check_geometry(int64_t T, int32_t H, int32_t D, int64_t N_pg, int32_t P, int
   if (h > D) return fail(SAWKV_EUNSUPPORTED, "h = %d exceeds D = %d", h, D);
   if (rot_mode != SAWKV_ROT_NONE && rot_mode != SAWKV_ROT_K && rot_mode != SAWKV_ROT_KV)
     return fail(SAWKV_EINVAL, "rot_mode = %d invalid", rot_mode);
+  if (H > 256) return fail(SAWKV_EUNSUPPORTED, "H = %d unsupported (at most 256)", H);
   if (T * (int64_t)H >= (INT64_C(1) << 31))
     return fail(SAWKV_EUNSUPPORTED, "T*H = %lld too large (< 2^31)", (long long)(T * H));
   if (slots == nullptr && T > 0) return fail(SAWKV_EINVAL, "slot_mapping is NULL");
@@ -304,6 +468,8 @@ int check_tensor(const char* name, const void* x, int64_t stride, const void* co
       return fail(SAWKV_EINVAL, "%s stride %lld < H*D = %d", name, (long long)stride, H * D);
     if (stride % 8 != 0)
       return fail(SAWKV_EALIGN, "%s stride %lld not a multiple of 8", name, (long long)stride);
+    if (stride >= (INT64_C(1) << 26))
+      return fail(SAWKV_EUNSUPPORTED, "%s stride %lld too large (< 2^26)", name, (long long)stride);
   }
   return SAWKV_OK;
 }
@@ -328,10 +494,19 @@ const void* const kGather[5][5] = SAWKV_TABLE(sawkv::gather_kernel);
 
 #undef SAWKV_TABLE
 
-int launch(const void* fn, int ntensors, int32_t TH, void* params, void* stream) {
+// One block = 4 waves = 64 vectors of one tensor.
+unsigned append_blocks(int32_t TH) {
+  return (unsigned)((TH + sawkv::kVecPerBlock - 1) / sawkv::kVecPerBlock);
+}
+
+// One gather block = 4 waves x 2 batches = 128 vectors of one tensor.
+unsigned gather_blocks(int32_t TH) {
+  return (unsigned)((TH + sawkv::kVecPerBlock - 1) / sawkv::kVecPerBlock);
+}
+
+int launch(const void* fn, int ntensors, unsigned blocks, void* params, void* stream) {
   if (fn == nullptr) return fail(SAWKV_EINVAL, "no kernel for this tensor/rotation combination");
-  const dim3 grid((unsigned)((TH + sawkv::kVecPerBlock - 1) / sawkv::kVecPerBlock),
-                  (unsigned)ntensors);
+  const dim3 grid(blocks, (unsigned)ntensors);
   void* args[] = {params};
   const hipError_t e = hipLaunchKernel(fn, grid, dim3(sawkv::kThreads), args, 0,
                                        reinterpret_cast<hipStream_t>(stream));
@@ -364,9 +539,11 @@ int append_impl(const void* k, const void* v, int64_t k_stride, int64_t v_stride
   }
   p.slots = slots;
   p.n_slots = N_pg * P;
+  p.T = (int32_t)T;
   p.TH = (int32_t)(T * H);
   p.H = H;
-  return launch(kAppend[hb[0]][hb[1]], n, p.TH, &p, stream);
+  p.h_magic = (uint32_t)(((1u << 20) + (uint32_t)H - 1u) / (uint32_t)H);
+  return launch(kAppend[hb[0]][hb[1]], n, append_blocks(p.TH), &p, stream);
 }
 
 int gather_impl(const void* k_codes, const void* v_codes, const void* k_scales,
@@ -394,9 +571,11 @@ int gather_impl(const void* k_codes, const void* v_codes, const void* k_scales,
   }
   p.slots = slots;
   p.n_slots = N_pg * P;
+  p.T = (int32_t)T;
   p.TH = (int32_t)(T * H);
   p.H = H;
-  return launch(kGather[hb[0]][hb[1]], n, p.TH, &p, stream);
+  p.h_magic = (uint32_t)(((1u << 20) + (uint32_t)H - 1u) / (uint32_t)H);
+  return launch(kGather[hb[0]][hb[1]], n, gather_blocks(p.TH), &p, stream);
 }
 
 }  // namespace
