@@ -85,6 +85,64 @@ def cpu_baseline(wl, h, rot, sample_tokens):
                       f"numpy float32 oracle, single thread"}
 
 
+def mse_gpu(torch, out, ref):
+    d = out.double() - ref.double()
+    return float((d * d).mean().item())
+
+
+def sweep_variants(S, torch, wl, kv, slots, timed, stream):
+    """Block size x rotation ablation on one tensor pair: time of the append
+    and reconstruction MSE of K and V after append + gather."""
+    k, v = kv
+    pools = S.alloc_pools(wl.N_pg, wl.P, wl.H, wl.D, k.device)
+    ko, vo = torch.empty_like(k), torch.empty_like(v)
+    res = []
+    bytes_call = wl.T * wl.bytes_per_token()
+    for h in (32, 64, 128):
+        for rot in ("none", "k", "kv"):
+            fn = lambda: S.quantize_append(k, v, slots, *pools, h=h, rot=rot, stream=stream)
+            for _ in range(20):
+                fn()
+            ms = float(np.median([timed(fn, 100) for _ in range(5)]))
+            S.dequant_gather(*pools, slots, h=h, rot=rot, k_out=ko, v_out=vo, stream=stream)
+            torch.cuda.synchronize()
+            res.append({"h": h, "rotation": rot, "append_us": round(ms * 1e3, 2),
+                        "GBps": round(bytes_call / (ms * 1e-3) / 1e9, 1),
+                        "mse_k": mse_gpu(torch, ko, k), "mse_v": mse_gpu(torch, vo, v)})
+    return res
+
+
+def decode_extras(torch, step_rot, timed, stream, wl, layers):
+    """Per-layer-call latency, and the same 36 calls replayed from one HIP
+    graph (launch overhead amortised)."""
+    eager_ms = timed(step_rot, 200)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step_rot()           # warm the side stream
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=side):
+        step_rot()
+    torch.cuda.synchronize()
+    for _ in range(20):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(side)
+    for _ in range(200):
+        g.replay()
+    e1.record(side)
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1) / 200
+    return {"layer_calls_per_step": layers,
+            "eager_us_per_step": round(eager_ms * 1e3, 2),
+            "eager_us_per_layer_call": round(eager_ms * 1e3 / layers, 3),
+            "graph_us_per_step": round(graph_ms * 1e3, 2),
+            "graph_us_per_layer_call": round(graph_ms * 1e3 / layers, 3),
+            "graph_tokens_per_s": round(wl.T / (graph_ms * 1e-3), 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,22 +181,21 @@ def main():
         del k, v
     pools = [S.alloc_pools(wl.N_pg, wl.P, wl.H, wl.D, dev) for _ in range(layers)]
     naive_pools = pools   # the control writes the same bytes to the same rows
-    stream = torch.cuda.current_stream()
+    stream = torch.cuda.current_stream()   # every launch below goes to the current stream
 
     def step_rot():
         for layer in range(layers):
             S.quantize_append(kvs[layer][0], kvs[layer][1], slots, *pools[layer], h=h,
-                              rot=ROT_NAME[rot], stream=stream)
+                              rot=ROT_NAME[rot])
 
     def step_naive():
         for layer in range(layers):
-            S.naive_int4_append(kvs[layer][0], kvs[layer][1], slots, *naive_pools[layer],
-                                stream=stream)
+            S.naive_int4_append(kvs[layer][0], kvs[layer][1], slots, *naive_pools[layer])
 
     def step_gather(outs):
         for layer in range(layers):
             S.dequant_gather(*pools[layer], slots, h=h, rot=ROT_NAME[rot],
-                             k_out=outs[layer][0], v_out=outs[layer][1], stream=stream)
+                             k_out=outs[layer][0], v_out=outs[layer][1])
 
     def timed(fn, n):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -177,12 +234,28 @@ def main():
         naive_ms.append(timed(step_naive, n_ab))
         rot_ms.append(timed(step_rot, n_ab))
     ratio = float(np.median(rot_ms) / np.median(naive_ms))
+    rng = np.random.default_rng(0)
+    boots = []
+    for _ in range(2000):
+        a = rng.choice(rot_ms, len(rot_ms))
+        b = rng.choice(naive_ms, len(naive_ms))
+        boots.append(np.median(a) / np.median(b))
+    ratio_ci = [round(float(np.percentile(boots, 2.5)), 4), round(float(np.percentile(boots, 97.5)), 4)]
 
     # read-back of the same slots
     outs = [(torch.empty_like(kvs[l][0]), torch.empty_like(kvs[l][1])) for l in range(layers)]
     for _ in range(3):
         step_gather(outs)
     g_ms = timed(lambda: step_gather(outs), max(20, args.steps // 2))
+
+    extra = {}
+    if args.workload == "sweep":
+        extra["variants"] = sweep_variants(S, torch, wl, kvs[0], slots, timed, stream)
+    if args.workload == "decode":
+        extra["decode"] = decode_extras(torch, step_rot, timed, stream, wl, layers)
+    if args.workload in ("sweep", "long", "prefill"):
+        ko, vo = outs[0]
+        extra["mse"] = {"k": mse_gpu(torch, ko, kvs[0][0]), "v": mse_gpu(torch, vo, kvs[0][1])}
 
     # attainable-bandwidth context on this machine: a 256 MiB device copy (torch)
     cbuf = torch.empty(64 * 1024 * 1024, dtype=torch.int32, device=dev)
@@ -222,6 +295,7 @@ def main():
         "vs_naive": {"rot_ms_median": round(float(np.median(rot_ms)), 5),
                      "naive_ms_median": round(float(np.median(naive_ms)), 5),
                      "rot_over_naive": round(ratio, 4),
+                     "rot_over_naive_ci95": ratio_ci,
                      "naive_GBps": round(bytes_step / (np.median(naive_ms) * 1e-3) / 1e9, 2),
                      "rounds": rounds, "steps_per_round": n_ab},
         "gather": {"ms_per_step": round(g_ms, 5),
@@ -230,6 +304,7 @@ def main():
         "attainable": {"copy_256MiB_GBps": round(copy_gbps, 1),
                        "note": "torch device-to-device copy on the same GPU, context only"},
         "kernel_source_hash": kernel_source_hash(),
+        **extra,
     }
     if not args.no_cpu:
         n = min(args.cpu_sample, wl.T)

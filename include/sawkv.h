@@ -45,7 +45,8 @@
  *   - Caller preconditions not checked: no two tokens of one call share a
  *     slot (which write wins is then unspecified); inputs, outputs and pools
  *     do not overlap; K/V values are finite.
- *   - Supported sizes: D = 128; h in {16, 32, 64, 128}; H >= 1; T*H < 2^31.
+ *   - Supported sizes: D = 128; h in {16, 32, 64, 128}; 1 <= H <= 256;
+ *     T*H < 2^31; token strides < 2^26 elements (SAWKV_EUNSUPPORTED otherwise).
  *   - Alignment: every tensor pointer 16-byte aligned, slot_mapping 8-byte
  *     aligned, token strides multiples of 8 elements.
  */

@@ -94,6 +94,8 @@ def gat(lib, **kw):
     (dict(rot=3), EINVAL),
     (dict(rot=-1), EINVAL),
     (dict(T=1 << 31, H=1), EUNSUPPORTED),
+    (dict(H=257, ks=257 * 128, vs=257 * 128), EUNSUPPORTED),
+    (dict(ks=1 << 26), EUNSUPPORTED),
     (dict(slots=None), EINVAL),
     (dict(slots=S + 4), EALIGN),
     (dict(slots=S + 4, T=0), EALIGN),

@@ -399,3 +399,40 @@ def test_sweep_workload(env, h, rot):
 def test_long_workload_round_trip(env):
     wl = _full(env, "long", n_sample=2048, gather=True)
     assert wl.T == wl.n_slots          # exact-fit pool: every slot written
+
+
+def test_graph_replay_matches_eager(env):
+    """Several layer calls captured in one HIP graph: every replay (with eager
+    work and synchronisation between replays) equals the eager result."""
+    torch, S = env
+    wl = W.WORKLOADS["decode"]
+    layers, n_pg, P = 4, 64, 16
+    rng = np.random.default_rng(77)
+    slots = rng.choice(n_pg * P, size=wl.T, replace=False).astype(np.int64)
+    sd = torch.from_numpy(slots).cuda()
+    kvs = [tuple(torch.from_numpy(a).cuda() for a in W.kv(wl, layer)) for layer in range(layers)]
+    eager = [gpu_pools(env, n_pg, P, wl.H, wl.D) for _ in range(layers)]
+    graph_pools = [gpu_pools(env, n_pg, P, wl.H, wl.D) for _ in range(layers)]
+    say("graph replay: capture", layers, "layer calls")
+    for layer in range(layers):
+        S.quantize_append(*kvs[layer], sd, *eager[layer], h=128, rot="k")
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for layer in range(layers):
+            S.quantize_append(*kvs[layer], sd, *graph_pools[layer], h=128, rot="k")
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for pools in graph_pools:                  # eager work between replays
+            pools[0].fill_(SENT_CODE)
+            pools[1].fill_(SENT_CODE)
+            pools[2].view(torch.int16).fill_(-1)
+            pools[3].view(torch.int16).fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(graph_pools, eager):
+            for x, y in zip(a, b):
+                assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f"replay {rep}"
