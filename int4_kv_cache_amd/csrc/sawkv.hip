@@ -138,10 +138,19 @@ __device__ __forceinline__ void quantize_store(const AppendTensor& A, const Appe
   for (int k = 0; k < kElems; ++k) m = fmaxf(m, fabsf(y[k]));
   m = fmaxf(m, quad_xor1(m));
   m = fmaxf(m, quad_xor2(m));
-  const float s32 = m / 7.0f;                         // IEEE division
+  // s32 = RN(amax / 7) by Markstein's correction with r7 = RN(1/7); the fma
+  // residual is exact, so the corrected quotient is the IEEE one
+  const float r7 = __builtin_bit_cast(float, 0x3E124925u);
+  const float q7 = m * r7;
+  const float s32 = __builtin_fmaf(__builtin_fmaf(-q7, 7.0f, m), r7, q7);
   const __half s16 = __float2half_rn(fminf(s32, 65504.0f));   // RNE, saturating
   const float sf = __half2float(s16);
-  const float r = sf > 0.0f ? 1.0f / sf : 0.0f;       // IEEE reciprocal
+  // r = RN(1/sf): the hardware reciprocal is within one ulp; one exact Newton
+  // step (residual by fma) rounds to RN(1/sf), because sf has at most 11
+  // significant bits and 1/sf is then never within 2^-35 (relative) of a
+  // float32 midpoint, while the corrected value is within 2^-46 of 1/sf
+  const float r0 = __builtin_amdgcn_rcpf(sf);
+  const float r = sf > 0.0f ? __builtin_fmaf(r0, __builtin_fmaf(-sf, r0, 1.0f), r0) : 0.0f;
   // clamp to [-8, 7] can bite only for a saturated or an f16-subnormal scale
   const bool need_clamp = (s32 > 65504.0f) || (sf < 6.103515625e-05f);
 

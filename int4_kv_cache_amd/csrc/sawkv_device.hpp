@@ -56,9 +56,10 @@ __device__ __forceinline__ float c_h() {
 }
 
 // Cross-lane butterfly on 8 registers. The leading s_nop covers the
-// "VALU writes a VGPR, DPP reads it" hazard for the first DPP read (the
-// compiler cannot see inside the asm); the trailing one covers DPP reads the
-// compiler emits right after the block.
+// "VALU writes a VGPR, DPP reads it" hazard (2 wait states) for the block's
+// DPP reads, which the compiler cannot see inside the asm. Registers written
+// by the block are DPP-read only by later blocks (which start with their own
+// s_nop) or by compiler-visible code, never right after the block.
 #define SAWKV_XBFLY8(NAME, PERM)                                                   \
   __device__ __forceinline__ void NAME(float& a0, float& a1, float& a2, float& a3, \
                                        float& a4, float& a5, float& a6, float& a7, \
@@ -72,8 +73,7 @@ __device__ __forceinline__ float c_h() {
         "v_fmac_f32_dpp %4, %4, %8 " PERM " row_mask:0xf bank_mask:0xf\n\t"        \
         "v_fmac_f32_dpp %5, %5, %8 " PERM " row_mask:0xf bank_mask:0xf\n\t"        \
         "v_fmac_f32_dpp %6, %6, %8 " PERM " row_mask:0xf bank_mask:0xf\n\t"        \
-        "v_fmac_f32_dpp %7, %7, %8 " PERM " row_mask:0xf bank_mask:0xf\n\t"        \
-        "s_nop 1"                                                                  \
+        "v_fmac_f32_dpp %7, %7, %8 " PERM " row_mask:0xf bank_mask:0xf"            \
         : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(a4), "+v"(a5), "+v"(a6),    \
           "+v"(a7)                                                                 \
         : "v"(sg));                                                                \
