@@ -113,8 +113,8 @@ def sweep_variants(S, torch, wl, kv, slots, timed, stream):
 
 
 def decode_extras(torch, step_rot, timed, stream, wl, layers):
-    """Per-layer-call latency, and the same 36 calls replayed from one HIP
-    graph (launch overhead amortised)."""
+    """For comparison with the one-launch step: one call per layer (eager),
+    and the same per-layer calls replayed from one HIP graph."""
     eager_ms = timed(step_rot, 200)
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
@@ -183,14 +183,20 @@ def main():
     naive_pools = pools   # the control writes the same bytes to the same rows
     stream = torch.cuda.current_stream()   # every launch below goes to the current stream
 
-    def step_rot():
+    def per_layer_rot():
         for layer in range(layers):
             S.quantize_append(kvs[layer][0], kvs[layer][1], slots, *pools[layer], h=h,
                               rot=ROT_NAME[rot])
 
-    def step_naive():
-        for layer in range(layers):
-            S.naive_int4_append(kvs[layer][0], kvs[layer][1], slots, *naive_pools[layer])
+    if layers > 1:
+        # a decode step: every layer's append in one launch (arguments marshalled once)
+        step_rot = S.LayersCall(kvs, slots, pools, h=h, rot=ROT_NAME[rot])
+        step_naive = S.LayersCall(kvs, slots, naive_pools, h=h, rot="none")
+    else:
+        step_rot = per_layer_rot
+
+        def step_naive():
+            S.naive_int4_append(kvs[0][0], kvs[0][1], slots, *naive_pools[0])
 
     def step_gather(outs):
         for layer in range(layers):
@@ -221,7 +227,7 @@ def main():
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     event_ms = e0.elapsed_time(e1) / args.steps
 
-    tokens = wl.T * layers
+    tokens = wl.T                      # new tokens per step (each appended to every layer)
     bytes_step = wl.T * wl.bytes_per_token() * layers
     gbps = bytes_step / (wall_ms * 1e-3) / 1e9
     achieved = bytes_step / (event_ms * 1e-3) / 1e9
@@ -252,7 +258,7 @@ def main():
     if args.workload == "sweep":
         extra["variants"] = sweep_variants(S, torch, wl, kvs[0], slots, timed, stream)
     if args.workload == "decode":
-        extra["decode"] = decode_extras(torch, step_rot, timed, stream, wl, layers)
+        extra["decode"] = decode_extras(torch, per_layer_rot, timed, stream, wl, layers)
     if args.workload in ("sweep", "long", "prefill"):
         ko, vo = outs[0]
         extra["mse"] = {"k": mse_gpu(torch, ko, kvs[0][0]), "v": mse_gpu(torch, vo, kvs[0][1])}
@@ -280,18 +286,22 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": describe(wl, h, rot), "tokens_per_step": tokens,
+                   "layers_appended_per_token": layers,
                    "heads": wl.H, "head_dim": wl.D, "block_size_h": h,
                    "rotation": ROT_NAME[rot], "page_size": wl.P, "pages": wl.N_pg,
                    "layers_per_step": layers, "parallelism": "single GPU"},
-        "step": "sawkv_quantize_append over the batch (rotate, token-wise INT4, pack, "
-                "paged scatter), one call per layer",
+        "step": ("sawkv_quantize_append_layers: every layer of the decode step in one launch"
+                 if layers > 1 else
+                 "sawkv_quantize_append over the batch (rotate, token-wise INT4, pack, "
+                 "paged scatter)"),
         "tokens_per_s": round(tokens / (wall_ms * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "algorithmic_bytes_per_launch": wl.T * wl.bytes_per_token(),
-                     "kernel": "sawkv::append_kernel"},
+                     "algorithmic_bytes_per_launch": bytes_step,
+                     "kernel": ("sawkv::append_layers_kernel" if layers > 1
+                                else "sawkv::append_kernel")},
         "vs_naive": {"rot_ms_median": round(float(np.median(rot_ms)), 5),
                      "naive_ms_median": round(float(np.median(naive_ms)), 5),
                      "rot_over_naive": round(ratio, 4),

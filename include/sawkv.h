@@ -101,6 +101,39 @@ int sawkv_quantize_append(const void* k, const void* v,
                           void* stream);
 
 /*
+ * Several layers of one decode step in one launch (up to SAWKV_MAX_LAYERS):
+ * the same computation as one sawkv_quantize_append call per layer, for
+ * layers that share T, H, D, the token strides, slot_mapping and the pool
+ * geometry (N_pg, P), each with its own K/V inputs and pools. Meant for
+ * decode, where one call per layer is bound by launch overhead; the
+ * decode-time append of every new token is the step the pages' fused kernel
+ * performs (youngju.dev fused-kernel diagram).
+ *
+ *   layers    HOST array of n_layers descriptors (read during the call only);
+ *             every layer must have k present, or every layer k absent (same
+ *             for v); absent tensors are NULL with NULL pools.
+ * Validation, ownership and stream behaviour as for sawkv_quantize_append.
+ */
+#define SAWKV_MAX_LAYERS 64
+
+typedef struct {
+  const void* k;         /* fp16 [T][H][D] of this layer, or NULL        */
+  const void* v;
+  void* k_codes;         /* uint8 [N_pg][P][H][D/2]                      */
+  void* v_codes;
+  void* k_scales;        /* fp16 [N_pg][P][H]                            */
+  void* v_scales;
+} sawkv_layer_t;
+
+int sawkv_quantize_append_layers(const sawkv_layer_t* layers, int32_t n_layers,
+                                 int64_t k_stride, int64_t v_stride,
+                                 const int64_t* slot_mapping, int64_t T,
+                                 int32_t H, int32_t D,
+                                 int64_t N_pg, int32_t P,
+                                 int32_t h, int32_t rot_mode,
+                                 void* stream);
+
+/*
  * Read the tokens at slot_mapping back from the pools: y = q * s, then (for
  * rotated tensors) the same normalised Sylvester transform, which is its own
  * inverse (youngju.dev reading, "The Rotation Trick": the rotation is

@@ -218,6 +218,42 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p) {
   else append_tensor<HB1>(p.t[1], p);
 }
 
+// Several layers of one decode step in one launch: every layer shares the
+// token count, heads, strides, slot mapping and pool geometry; blockIdx.y
+// enumerates (layer, tensor). The per-layer pointers travel in the kernel
+// arguments, so the call needs no device-side descriptor.
+constexpr int kMaxLayers = 64;
+
+struct LayerPtrs {
+  const __half* k;
+  const __half* v;
+  uint8_t* k_codes;
+  uint8_t* v_codes;
+  __half* k_scales;
+  __half* v_scales;
+};
+
+struct LayersParams {
+  AppendParams common;   // its t[] are unused
+  int64_t k_stride, v_stride;
+  int32_t n_tensors;     // 1 or 2 per layer
+  int32_t only_v;        // n_tensors == 1 and that tensor is V
+  LayerPtrs layer[kMaxLayers];
+};
+
+static_assert(sizeof(LayersParams) <= 4096, "kernel arguments must stay within 4 KB");
+
+template <int HB0, int HB1>
+__global__ __launch_bounds__(kThreads) void append_layers_kernel(LayersParams p) {
+  const int slot_in_layer = (int)(blockIdx.y % (unsigned)p.n_tensors);
+  const LayerPtrs& L = p.layer[blockIdx.y / (unsigned)p.n_tensors];
+  const bool is_v = p.n_tensors == 2 ? slot_in_layer == 1 : p.only_v != 0;
+  const AppendTensor A = is_v ? AppendTensor{L.v, p.v_stride, L.v_codes, L.v_scales}
+                              : AppendTensor{L.k, p.k_stride, L.k_codes, L.k_scales};
+  if (slot_in_layer == 0) append_tensor<HB0>(A, p.common);
+  else append_tensor<HB1>(A, p.common);
+}
+
 // ---------------------------------------------------------------------------
 // gather: pool -> dequantise -> inverse rotation -> fp16
 // ---------------------------------------------------------------------------
@@ -499,6 +535,7 @@ int hb_index(int32_t h, bool rot) {
    {(void*)&K<128, 0>, nullptr, nullptr, nullptr, (void*)&K<128, 128>}}
 
 const void* const kAppend[5][5] = SAWKV_TABLE(sawkv::append_kernel);
+const void* const kAppendLayers[5][5] = SAWKV_TABLE(sawkv::append_layers_kernel);
 const void* const kGather[5][5] = SAWKV_TABLE(sawkv::gather_kernel);
 
 #undef SAWKV_TABLE
@@ -513,9 +550,9 @@ unsigned gather_blocks(int32_t TH) {
   return (unsigned)((TH + sawkv::kVecPerBlock - 1) / sawkv::kVecPerBlock);
 }
 
-int launch(const void* fn, int ntensors, unsigned blocks, void* params, void* stream) {
+int launch(const void* fn, int grid_y, unsigned blocks, void* params, void* stream) {
   if (fn == nullptr) return fail(SAWKV_EINVAL, "no kernel for this tensor/rotation combination");
-  const dim3 grid(blocks, (unsigned)ntensors);
+  const dim3 grid(blocks, (unsigned)grid_y);
   void* args[] = {params};
   const hipError_t e = hipLaunchKernel(fn, grid, dim3(sawkv::kThreads), args, 0,
                                        reinterpret_cast<hipStream_t>(stream));
@@ -553,6 +590,54 @@ int append_impl(const void* k, const void* v, int64_t k_stride, int64_t v_stride
   p.H = H;
   p.h_magic = (uint32_t)(((1u << 20) + (uint32_t)H - 1u) / (uint32_t)H);
   return launch(kAppend[hb[0]][hb[1]], n, append_blocks(p.TH), &p, stream);
+}
+
+int append_layers_impl(const sawkv_layer_t* layers, int32_t n_layers, int64_t k_stride,
+                       int64_t v_stride, const int64_t* slots, int64_t T, int32_t H, int32_t D,
+                       int64_t N_pg, int32_t P, int32_t h, int32_t rot_mode, void* stream) {
+  int st = check_geometry(T, H, D, N_pg, P, h, rot_mode, slots);
+  if (st) return st;
+  if (layers == nullptr) return fail(SAWKV_EINVAL, "layers is NULL");
+  if (n_layers < 1 || n_layers > sawkv::kMaxLayers)
+    return fail(SAWKV_EINVAL, "n_layers = %d outside [1, %d]", n_layers, sawkv::kMaxLayers);
+  if (T == 0) return ok();
+  const bool has_k = layers[0].k != nullptr, has_v = layers[0].v != nullptr;
+  if (!has_k && !has_v) return fail(SAWKV_EINVAL, "layer 0 has neither k nor v");
+  sawkv::LayersParams p{};
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const sawkv_layer_t& L = layers[l];
+    if ((L.k != nullptr) != has_k || (L.v != nullptr) != has_v)
+      return fail(SAWKV_EINVAL, "layer %d: k/v presence differs from layer 0", l);
+    for (int t = 0; t < 2; ++t) {
+      const bool present = t == 0 ? has_k : has_v;
+      if (!present) continue;
+      st = t == 0 ? check_tensor("k", L.k, k_stride, L.k_codes, L.k_scales, H, D)
+                  : check_tensor("v", L.v, v_stride, L.v_codes, L.v_scales, H, D);
+      if (st) {
+        char detail[sizeof g_err];
+        snprintf(detail, sizeof detail, "%s", g_err);
+        return fail(st, "layer %d: %s", l, detail);
+      }
+    }
+    p.layer[l] = {static_cast<const __half*>(L.k), static_cast<const __half*>(L.v),
+                  static_cast<uint8_t*>(L.k_codes), static_cast<uint8_t*>(L.v_codes),
+                  static_cast<__half*>(L.k_scales), static_cast<__half*>(L.v_scales)};
+  }
+  int n = 0, hb[2] = {0, 0};
+  if (has_k) hb[n++] = hb_index(h, rot_mode != SAWKV_ROT_NONE);
+  if (has_v) hb[n++] = hb_index(h, rot_mode == SAWKV_ROT_KV);
+  p.n_tensors = n;
+  p.only_v = (!has_k && has_v) ? 1 : 0;
+  p.k_stride = k_stride;
+  p.v_stride = v_stride;
+  p.common.slots = slots;
+  p.common.n_slots = N_pg * P;
+  p.common.T = (int32_t)T;
+  p.common.TH = (int32_t)(T * H);
+  p.common.H = H;
+  p.common.h_magic = (uint32_t)(((1u << 20) + (uint32_t)H - 1u) / (uint32_t)H);
+  return launch(kAppendLayers[hb[0]][hb[1]], n * n_layers, append_blocks(p.common.TH), &p,
+                stream);
 }
 
 int gather_impl(const void* k_codes, const void* v_codes, const void* k_scales,
@@ -598,6 +683,15 @@ int sawkv_quantize_append(const void* k, const void* v, int64_t k_stride, int64_
                           void* stream) {
   return append_impl(k, v, k_stride, v_stride, slot_mapping, T, H, D, k_codes, v_codes,
                      k_scales, v_scales, N_pg, P, h, rot_mode, stream);
+}
+
+int sawkv_quantize_append_layers(const sawkv_layer_t* layers, int32_t n_layers,
+                                 int64_t k_stride, int64_t v_stride,
+                                 const int64_t* slot_mapping, int64_t T, int32_t H, int32_t D,
+                                 int64_t N_pg, int32_t P, int32_t h, int32_t rot_mode,
+                                 void* stream) {
+  return append_layers_impl(layers, n_layers, k_stride, v_stride, slot_mapping, T, H, D, N_pg,
+                            P, h, rot_mode, stream);
 }
 
 int sawkv_dequant_gather(const void* k_codes, const void* v_codes, const void* k_scales,

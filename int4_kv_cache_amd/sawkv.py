@@ -25,9 +25,22 @@ ROT = {"none": ROT_NONE, "k": ROT_K, "kv": ROT_KV}
 
 _p, _i64, _i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
 
+
+class LayerDesc(ctypes.Structure):
+    """sawkv_layer_t"""
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+                ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p)]
+
+
+MAX_LAYERS = 64
+
 lib.sawkv_quantize_append.argtypes = [_p, _p, _i64, _i64, _p, _i64, _i32, _i32,
                                       _p, _p, _p, _p, _i64, _i32, _i32, _i32, _p]
 lib.sawkv_quantize_append.restype = ctypes.c_int
+lib.sawkv_quantize_append_layers.argtypes = [ctypes.POINTER(LayerDesc), _i32, _i64, _i64, _p,
+                                             _i64, _i32, _i32, _i64, _i32, _i32, _i32, _p]
+lib.sawkv_quantize_append_layers.restype = ctypes.c_int
 lib.sawkv_dequant_gather.argtypes = [_p, _p, _p, _p, _i64, _i32, _p, _i64, _i32, _i32,
                                      _p, _p, _i32, _i32, _p]
 lib.sawkv_dequant_gather.restype = ctypes.c_int
@@ -124,6 +137,62 @@ def quantize_append(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, *,
         _addr(k_codes) if k is not None else None, _addr(v_codes) if v is not None else None,
         _addr(k_scales) if k is not None else None, _addr(v_scales) if v is not None else None,
         N_pg, P, h, _rot(rot), _stream(stream)))
+
+
+def quantize_append_layers(kv, slot_mapping, pools, *, h=128, rot="kv", stream=None):
+    """One launch for several layers of a decode step
+    (sawkv_quantize_append_layers). kv: list of (k, v) per layer (k or v may
+    be None in every layer); pools: list of (k_codes, v_codes, k_scales,
+    v_scales) per layer; all layers share shapes, strides and slot_mapping."""
+    LayersCall(kv, slot_mapping, pools, h=h, rot=rot)(stream)
+
+
+class LayersCall:
+    """sawkv_quantize_append_layers with its arguments checked and marshalled
+    once: calling the object only launches (for decode loops, where per-call
+    Python work would otherwise exceed the kernel time). The tensors must stay
+    alive and keep their storage while the object is used."""
+
+    def __init__(self, kv, slot_mapping, pools, *, h=128, rot="kv"):
+        self._args = _layers_args(kv, slot_mapping, pools, h, rot)
+        self._keep = (kv, slot_mapping, pools)
+
+    def __call__(self, stream=None):
+        descs, n, ks_, vs_, slots, T, H, D, N_pg, P, h, rot = self._args
+        _check(lib.sawkv_quantize_append_layers(descs, n, ks_, vs_, slots, T, H, D, N_pg, P, h,
+                                                rot, _stream(stream)))
+
+
+def _layers_args(kv, slot_mapping, pools, h, rot):
+    n = len(kv)
+    if n != len(pools) or not 1 <= n <= MAX_LAYERS:
+        raise ValueError(f"need 1..{MAX_LAYERS} layers with one pool set each")
+    k0, v0 = kv[0]
+    ref = k0 if k0 is not None else v0
+    T, H, D, _ = _kv_geometry(ref)
+    ks_ = _kv_geometry(k0)[3] if k0 is not None else 0
+    vs_ = _kv_geometry(v0)[3] if v0 is not None else 0
+    pool = _pool_geometry(pools[0][0], pools[0][2]) if k0 is not None else \
+        _pool_geometry(pools[0][1], pools[0][3])
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must be int64 [T]")
+    descs = (LayerDesc * n)()
+    for i, ((k, v), (kc, vc, kss, vss)) in enumerate(zip(kv, pools)):
+        # the C call takes one geometry for all layers: insist on it here
+        if (k is None) != (k0 is None) or (v is None) != (v0 is None):
+            raise ValueError("every layer must have the same k/v presence")
+        for x, stride in ((k, ks_), (v, vs_)):
+            if x is not None and _kv_geometry(x) != (T, H, D, stride):
+                raise ValueError("every layer must have the same [T, H, D] and stride")
+        for codes, scales, present in ((kc, kss, k is not None), (vc, vss, v is not None)):
+            if present and tuple(_pool_geometry(codes, scales)) != tuple(pool):
+                raise ValueError("every layer's pools must have the same shape")
+        descs[i] = LayerDesc(_addr(k), _addr(v),
+                             _addr(kc) if k is not None else None,
+                             _addr(vc) if v is not None else None,
+                             _addr(kss) if k is not None else None,
+                             _addr(vss) if v is not None else None)
+    return (descs, n, ks_, vs_, _addr(slot_mapping), T, H, D, pool[0], pool[1], h, _rot(rot))
 
 
 def naive_int4_append(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, *,

@@ -24,6 +24,11 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(sawkv_\w+)\s*\(", text)))
 
 
+class LayerDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("k", "v", "k_codes", "v_codes", "k_scales", "v_scales")]
+
+
 @pytest.fixture(scope="module")
 def lib():
     L = ctypes.CDLL(LIB)
@@ -34,6 +39,8 @@ def lib():
     L.sawkv_naive_int4_append.argtypes = [p, p, i64, i64, p, i64, i32, i32, p, p, p, p, i64,
                                           i32, p]
     L.sawkv_naive_int4_gather.argtypes = [p, p, p, p, i64, i32, p, i64, i32, i32, p, p, p]
+    L.sawkv_quantize_append_layers.argtypes = [ctypes.POINTER(LayerDesc), i32, i64, i64, p, i64,
+                                               i32, i32, i64, i32, i32, i32, p]
     L.sawkv_status_string.restype = ctypes.c_char_p
     L.sawkv_last_error.restype = ctypes.c_char_p
     return L
@@ -149,3 +156,35 @@ def test_one_tensor_may_be_absent(lib):
     # V absent: its pool pointers are ignored (T = 0 keeps this launch-free)
     assert app(lib, T=0, v=None, vc=None, vss=None) == OK
     assert gat(lib, T=0, ko=None, kc=None, kss=None) == OK
+
+
+def layers_call(lib, descs, n=None, T=256, slots=S, h=128, rot=1):
+    arr = (LayerDesc * max(1, len(descs)))(*descs)
+    return lib.sawkv_quantize_append_layers(arr if descs else None, len(descs) if n is None else n,
+                                            1024, 1024, slots, T, 8, 128, 64, 16, h, rot, None)
+
+
+def good_layer(i):
+    base = A * (16 + 8 * i)
+    return LayerDesc(base, base + A, base + 2 * A, base + 3 * A, base + 4 * A, base + 5 * A)
+
+
+def test_layers_validation(lib):
+    descs = [good_layer(i) for i in range(4)]
+    assert layers_call(lib, [], n=0) == EINVAL                        # NULL array
+    assert layers_call(lib, descs, n=0) == EINVAL
+    assert layers_call(lib, [good_layer(i) for i in range(65)]) == EINVAL
+    bad = list(descs)
+    bad[2] = LayerDesc(bad[2].k, None, bad[2].k_codes, None, bad[2].k_scales, None)
+    assert layers_call(lib, bad) == EINVAL                            # presence differs
+    assert b"layer 2" in lib.sawkv_last_error()
+    mis = list(descs)
+    mis[3] = LayerDesc(mis[3].k + 8, mis[3].v, mis[3].k_codes, mis[3].v_codes,
+                       mis[3].k_scales, mis[3].v_scales)
+    assert layers_call(lib, mis) == EALIGN
+    assert b"layer 3" in lib.sawkv_last_error()
+    nul = list(descs)
+    nul[1] = LayerDesc(nul[1].k, nul[1].v, None, nul[1].v_codes, nul[1].k_scales, nul[1].v_scales)
+    assert layers_call(lib, nul) == EINVAL
+    assert layers_call(lib, descs, h=40) == EUNSUPPORTED
+    assert layers_call(lib, descs, T=0) == OK                          # nothing launched

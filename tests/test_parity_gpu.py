@@ -436,3 +436,37 @@ def test_graph_replay_matches_eager(env):
         for a, b in zip(graph_pools, eager):
             for x, y in zip(a, b):
                 assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f"replay {rep}"
+
+
+@pytest.mark.parametrize("n_layers,rot,drop", [(36, "k", None), (64, "kv", None),
+                                                (5, "kv", "v"), (3, "none", "k")])
+def test_layers_call_equals_per_layer_calls(env, n_layers, rot, drop):
+    """One sawkv_quantize_append_layers launch == one call per layer."""
+    torch, S = env
+    wl = W.WORKLOADS["decode"]
+    n_pg, P = 40, 16
+    rng = np.random.default_rng(n_layers)
+    slots = rng.choice(n_pg * P, size=wl.T, replace=False).astype(np.int64)
+    slots[:3] = [-1, n_pg * P, n_pg * P + 100]                     # skipped tokens
+    sd = torch.from_numpy(slots).cuda()
+    say(f"layers call: {n_layers} layers rot={rot} drop={drop}")
+    kv = []
+    for layer in range(n_layers):
+        k, v = (torch.from_numpy(a).cuda() for a in W.kv(wl, layer % wl.layers))
+        kv.append((None if drop == "k" else k, None if drop == "v" else v))
+    one = [gpu_pools(env, n_pg, P, wl.H, wl.D) for _ in range(n_layers)]
+    per = [gpu_pools(env, n_pg, P, wl.H, wl.D) for _ in range(n_layers)]
+    S.quantize_append_layers(kv, sd, one, h=128, rot=rot)
+    for layer in range(n_layers):
+        S.quantize_append(*kv[layer], sd, *per[layer], h=128, rot=rot)
+    torch.cuda.synchronize()
+    for a, b in zip(one, per):
+        for x, y in zip(a, b):
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+    # and the first layer against the oracle
+    want = np_pools(n_pg, P, wl.H, wl.D)
+    k0 = None if drop == "k" else W.kv(wl, 0)[0]
+    v0 = None if drop == "v" else W.kv(wl, 0)[1]
+    O.quantize_append(k0, v0, slots, *want, h=128,
+                      rot_mode={"none": O.ROT_NONE, "k": O.ROT_K, "kv": O.ROT_KV}[rot])
+    assert_pools_equal([to_np(x) for x in one[0]], want, "layers call layer 0")
