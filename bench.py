@@ -98,7 +98,7 @@ def sweep_variants(S, torch, wl, kv, slots, timed, stream):
     ko, vo = torch.empty_like(k), torch.empty_like(v)
     res = []
     bytes_call = wl.T * wl.bytes_per_token()
-    for h in (32, 64, 128):
+    for h in (16, 32, 64, 128):
         for rot in ("none", "k", "kv"):
             fn = lambda: S.quantize_append(k, v, slots, *pools, h=h, rot=rot, stream=stream)
             for _ in range(20):
