@@ -34,6 +34,25 @@ Draw recipe (numpy PCG64 via default_rng, seeded from a SeedSequence key):
   slots     key (seed, workload id, 2)
 Any token range of any tensor can be regenerated on its own, which is what the
 full-size tests use to check sampled tokens.
+
+Decode attention over the paged INT4 cache reads a pool that is already full;
+its inputs (AttnWorkload, attn_inputs) are drawn directly as pool contents:
+codes, fp16 scales, fp16 queries, block tables and context lengths. They are
+not produced by the write path, so no attention input comes out of the kernels
+under test. Recipe, key (seed, workload id, 3, part[, chunk]):
+  lengths   part 0: integers uniform in [lo, hi] (or a fixed list)
+  pages     part 1: a permutation of the pool; sequence b takes the next
+            ceil(L_b / P) pages; unused table entries are -1; with
+            masked > 0 that many in-range entries (chosen uniformly) are set
+            to -1 as well
+  codes     part 2 (K) / 3 (V), per chunk of 4096 pages: every nibble drawn
+            independently from 0.96 x a discretised normal on [-8, 7] with
+            sd 2.7 (the spread of codes of a rotated vector whose largest
+            entry maps to 7) + 0.04 x uniform on [-8, 7] (so that every code,
+            -8 included, occurs), sampled through a 65536-entry byte table
+  scales    part 4 (K) / 5 (V): fp16 of base[head] * lognormal(0, 0.3), base
+            0.35, and 20x that on two heads per tensor (outlier heads)
+  queries   part 6: fp16 standard normal [B, Hq, D]
 """
 
 import os
@@ -192,3 +211,127 @@ def slot_mapping(wl):
 def pool_shapes(N_pg, P, H, D):
     """Shapes and dtypes of the four pool arrays (K codes, V codes, K scales, V scales)."""
     return ((N_pg, P, H, D // 2), np.uint8), ((N_pg, P, H), np.float16)
+
+
+# --------------------------------------------------------------------------
+# Decode attention over a filled INT4 pool
+# --------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class AttnWorkload:
+    name: str
+    wid: int
+    B: int                 # sequences, one query token each
+    Hq: int                # query heads
+    H: int                 # KV heads (Hq % H == 0)
+    D: int
+    P: int                 # page size
+    ctx: tuple             # ("uniform", lo, hi) | ("list", (L0, L1, ...))
+    h: int                 # Hadamard block size the pool was written with
+    rot_mode: int
+    spare_pages: int = 64  # pool pages no sequence uses
+    masked: int = 0        # in-range block-table entries replaced by -1
+    seed: int = 0
+
+    @property
+    def G(self):
+        return self.Hq // self.H
+
+    def bytes_per_token(self):
+        """Algorithmic HBM bytes per cached token read by one decode step:
+        K and V codes and fp16 scales of every KV head."""
+        return self.H * (2 * (self.D // 2) + 2 * 2)
+
+
+ATTN_WORKLOADS = {
+    # The decode workload's shape (256 concurrent requests, 8 KV heads of
+    # 128, page 16, K-only rotation) with 32 query heads (4 per KV head) and
+    # contexts of 1 to 8000 tokens.
+    "attn": AttnWorkload("attn", 6, 256, 32, 8, 128, 16, ("uniform", 1, 8000), 128, ROT_K),
+    # Small cases the oracle finishes in seconds: ragged lengths around the
+    # 16-token tiles and 32-token steps, an empty context and masked pages.
+    "attn_small": AttnWorkload("attn_small", 7, 9, 32, 8, 128, 16,
+                               ("list", (0, 1, 15, 16, 17, 33, 100, 700, 1300)), 128,
+                               ROT_KV, masked=3),
+}
+
+
+def attn_lengths(wl):
+    kind = wl.ctx[0]
+    if kind == "uniform":
+        rng = np.random.default_rng([wl.seed, wl.wid, 3, 0])
+        return rng.integers(wl.ctx[1], wl.ctx[2] + 1, size=wl.B).astype(np.int32)
+    if kind == "list":
+        L = np.asarray(wl.ctx[1], dtype=np.int32)
+        if len(L) != wl.B:
+            raise ValueError("length list does not match B")
+        return L
+    raise ValueError(kind)
+
+
+def _code_table():
+    """uint8 [65536]: a 16-bit uniform draw -> one code byte whose two nibbles
+    are independent draws from the code distribution described above."""
+    v = np.arange(-8, 8, dtype=np.float64)
+    w = np.exp(-0.5 * (v / 2.7) ** 2)
+    w = 0.96 * w / w.sum() + 0.04 / 16.0
+    cdf = np.cumsum(w)
+    u = (np.arange(256, dtype=np.float64) + 0.5) / 256.0
+    nib = np.searchsorted(cdf, u).clip(0, 15) - 8          # [256] value for each byte draw
+    lo = (nib.astype(np.int64) & 0xF)
+    hi = (nib.astype(np.int64) & 0xF)
+    idx = np.arange(65536)
+    return (lo[idx & 0xFF] | (hi[idx >> 8] << 4)).astype(np.uint8)
+
+
+def attn_inputs(wl):
+    """Seeded inputs of one decode-attention step. Returns a dict of numpy
+    arrays: q fp16 [B, Hq, D]; k_codes, v_codes uint8 [N_pg, P, H, D/2];
+    k_scales, v_scales fp16 [N_pg, P, H]; block_tables int32 [B, max_pages];
+    context_lens int32 [B]."""
+    L = attn_lengths(wl)
+    npages = -(-L.astype(np.int64) // wl.P)
+    N_pg = int(npages.sum()) + wl.spare_pages
+    max_pages = max(1, int(npages.max()) if len(npages) else 1)
+    rng = np.random.default_rng([wl.seed, wl.wid, 3, 1])
+    perm = rng.permutation(N_pg).astype(np.int32)
+    bt = np.full((wl.B, max_pages), -1, dtype=np.int32)
+    start = np.concatenate([[0], np.cumsum(npages)[:-1]]).astype(np.int64)
+    for b in range(wl.B):
+        bt[b, :npages[b]] = perm[start[b]:start[b] + npages[b]]
+    if wl.masked:
+        live = np.argwhere(np.arange(max_pages)[None, :] < npages[:, None])
+        pick = rng.choice(len(live), size=min(wl.masked, len(live)), replace=False)
+        bt[live[pick, 0], live[pick, 1]] = -1
+
+    table = _code_table()
+    half = wl.D // 2
+    codes = []
+    for part in (2, 3):
+        out = np.empty((N_pg, wl.P, wl.H, half), dtype=np.uint8)
+        flat = out.reshape(N_pg, -1)
+        per = 4096
+
+        def fill(c, part=part, flat=flat):
+            lo, hi = c * per, min(N_pg, (c + 1) * per)
+            r = np.random.default_rng([wl.seed, wl.wid, 3, part, c])
+            draw = r.integers(0, 65536, size=(hi - lo, flat.shape[1]), dtype=np.uint16)
+            flat[lo:hi] = table[draw]
+
+        n_chunks = -(-N_pg // per)
+        with ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(fill, range(n_chunks)))
+        codes.append(out)
+
+    scales = []
+    for part in (4, 5):
+        r = np.random.default_rng([wl.seed, wl.wid, 3, part])
+        base = np.full(wl.H, 0.35, dtype=np.float64)
+        base[r.choice(wl.H, size=min(2, wl.H), replace=False)] *= 20.0
+        ln = r.lognormal(0.0, 0.3, size=(N_pg, wl.P, wl.H))
+        scales.append((ln * base[None, None, :]).astype(np.float16))
+
+    r = np.random.default_rng([wl.seed, wl.wid, 3, 6])
+    q = r.standard_normal((wl.B, wl.Hq, wl.D), dtype=np.float32).astype(np.float16)
+    return {"q": q, "k_codes": codes[0], "v_codes": codes[1], "k_scales": scales[0],
+            "v_scales": scales[1], "block_tables": bt, "context_lens": L}

@@ -9,6 +9,7 @@ tests/test_oracle_pins.py; every function here is pinned.
 """
 from .sawint4 import (  # noqa: F401
     F16_MAX, ROT_K, ROT_KV, ROT_NONE, c_h, decode_vectors, dequant_gather,
-    encode_vectors, fwht_blocks, mse, pack_nibbles, quantize,
+    dequant_exact, encode_vectors, fwht_blocks, mse, pack_nibbles,
+    paged_decode_attention, quantize,
     quantize_append, quantize_with_scale, rotate, token_scale, unpack_nibbles,
 )

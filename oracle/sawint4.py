@@ -250,3 +250,69 @@ def mse(x_hat, x):
     """Mean squared reconstruction error, in float64, over all elements."""
     d = np.asarray(x_hat, dtype=np.float64) - np.asarray(x, dtype=np.float64)
     return float(np.mean(d * d))
+
+
+# --------------------------------------------------------------------------
+# Consumer of the pages: decode attention over the INT4 pool
+# --------------------------------------------------------------------------
+
+def dequant_exact(codes, s16, h, rotate_it):
+    """Dequantised vectors in float64 without any final rounding: q * s, then
+    (rotated tensors) the normalised Sylvester transform, its own inverse.
+    The partial sums of F(q * s) are exact in float32; the 1/sqrt(h) factor is
+    applied in float64."""
+    q = unpack_nibbles(codes).astype(F32)
+    y = q * np.asarray(s16, dtype=F16).astype(F32)[..., None]
+    if rotate_it:
+        return fwht_blocks(y, h).astype(np.float64) / np.sqrt(np.float64(h))
+    return y.astype(np.float64)
+
+
+def paged_decode_attention(q, k_codes, k_scales, v_codes, v_scales, block_tables,
+                           context_lens, h=128, rot_mode=ROT_KV, sm_scale=None):
+    """One decode step of attention over the paged INT4 cache, in float64.
+
+    q             fp16 [B, Hq, D]; query head j reads KV head j // (Hq // H)
+    k/v pools     as written by quantize_append
+    block_tables  int [B, max_pages]: page of the sequence's p-th block
+    context_lens  int [B]: tokens 0..L-1 live at page block_tables[b, t // P],
+                  offset t % P; a page id outside the pool masks its tokens
+    Returns float64 [B, Hq, D]: softmax(sm_scale * q . K_t) weighted sum of
+    V_t over the context, with K_t, V_t the dequantised vectors in the
+    original basis; an empty context gives zeros.
+
+    The consumer of the paged INT4 cache: youngju.dev English page, "Why the
+    KV Cache Is the Real Bottleneck" (decoding reads every cached K and V;
+    serving engines keep paged layouts and fused attention), and ainews.cool,
+    "技术深度解析" item 3 (dequantisation back to compute precision is
+    normally fused into the attention kernel). The K and V rows are the
+    exact dequantised vectors, so this is the plain definition of one decode
+    step of softmax attention over them.
+    """
+    q = np.asarray(q, dtype=F16)
+    B, Hq, D = q.shape
+    n_pg, P, H, half = k_codes.shape
+    G = Hq // H
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(D)
+    kc = k_codes.reshape(n_pg * P, H, half)
+    vc = v_codes.reshape(n_pg * P, H, half)
+    ks = k_scales.reshape(n_pg * P, H)
+    vs = v_scales.reshape(n_pg * P, H)
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        L = int(context_lens[b])
+        t = np.arange(L)
+        pages = np.asarray(block_tables[b], dtype=np.int64)[t // P]
+        ok = (pages >= 0) & (pages < n_pg)
+        slots = (pages * P + t % P)[ok]
+        if len(slots) == 0:
+            continue
+        K = dequant_exact(kc[slots], ks[slots], h, _rotated(rot_mode, "k"))   # [n, H, D]
+        V = dequant_exact(vc[slots], vs[slots], h, _rotated(rot_mode, "v"))
+        for j in range(Hq):
+            kv = j // G
+            s = (K[:, kv, :] @ q[b, j].astype(np.float64)) * np.float64(sm_scale)
+            w = np.exp(s - s.max())
+            out[b, j] = (w / w.sum()) @ V[:, kv, :]
+    return out
