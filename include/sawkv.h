@@ -53,6 +53,7 @@
 #ifndef SAWKV_H
 #define SAWKV_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -175,6 +176,61 @@ int sawkv_naive_int4_gather(const void* k_codes, const void* v_codes,
                             int32_t H, int32_t D,
                             void* k_out, void* v_out,
                             void* stream);
+
+/*
+ * Decode attention over the paged INT4 pools: one new query token per
+ * sequence attends to every cached token of its sequence. This is the consumer
+ * the pages fuse dequantisation into (ainews.cool, "技术深度解析" item 3:
+ * dequantisation normally fused with the attention kernel; youngju.dev
+ * English page, "Why the KV Cache Is the Real Bottleneck": paged layouts and
+ * fused attention must be kept). Computed, for sequence b and query head j
+ * (KV head j / G, G = Hq / H):
+ *
+ *   K_t, V_t = the dequantised rows of token t in the original basis
+ *              (q * s, then the inverse rotation for rotated tensors)
+ *   out[b][j] = sum_t softmax_t(sm_scale * q[b][j] . K_t) V_t,  fp16
+ *
+ * over t < min(context_lens[b], max_context); token t lives in page
+ * block_tables[b][t / P] at offset t % P. A page id < 0 or >= N_pg masks the
+ * page's tokens (nothing is read there); an empty or fully masked context
+ * gives a zero row. Keys are never un-rotated: the query is rotated once,
+ * since the rotation is orthogonal (youngju.dev, "The Rotation Trick").
+ *
+ *   q             fp16 [B][Hq][D]; sequence b's row starts at q + b*q_stride
+ *                 elements (q_stride >= Hq*D, a multiple of 8)
+ *   pools         as written by sawkv_quantize_append with the same h and
+ *                 rot_mode (SAWKV_ROT_K: V naive; SAWKV_ROT_KV: both rotated)
+ *   block_tables  int32 [B][bt_stride], bt_stride >= ceil(max_context / P);
+ *                 entries past a sequence's last page are never read
+ *   context_lens  int32 [B], device memory; values above max_context are
+ *                 cut to max_context, negative values count as 0
+ *   out           fp16 [B][Hq][D] contiguous
+ *   workspace     device memory of at least the size that
+ *                 sawkv_decode_attention_workspace_size reports for the same
+ *                 B, Hq, H, D, max_context; 256-byte aligned; owned by the
+ *                 caller and overwritten by the call (one call at a time per
+ *                 workspace)
+ * Supported: D = 128; Hq / H in {1, 2, 4, 8}; H <= 256; P a multiple of 16;
+ * h in {16, 32, 64, 128}; N_pg < 2^31; max_context <= 2^30; B <= 2^24
+ * (SAWKV_EUNSUPPORTED otherwise). B == 0 returns SAWKV_OK without reading
+ * any pointer. Numerics: float32 accumulation from exact products of the
+ * INT4 codes with fp16 hi + lo splits of the query and of the softmax
+ * weights; the result is within a few fp16 ulps of the exact attention.
+ */
+int sawkv_decode_attention_workspace_size(int64_t B, int32_t Hq, int32_t H, int32_t D,
+                                          int64_t max_context, size_t* bytes);
+
+int sawkv_decode_attention(const void* q, int64_t q_stride,
+                           const void* k_codes, const void* v_codes,
+                           const void* k_scales, const void* v_scales,
+                           int64_t N_pg, int32_t P,
+                           const int32_t* block_tables, int64_t bt_stride,
+                           const int32_t* context_lens,
+                           int64_t B, int32_t Hq, int32_t H, int32_t D,
+                           int64_t max_context, float sm_scale,
+                           int32_t h, int32_t rot_mode,
+                           void* out, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* sawkv_status_string(int status);

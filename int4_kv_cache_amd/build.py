@@ -2,7 +2,8 @@
 
     python -m int4_kv_cache_amd.build
 
-Compiles int4_kv_cache_amd/csrc/sawkv.hip into int4_kv_cache_amd/libsawkv.so.
+Compiles int4_kv_cache_amd/csrc/sawkv.hip (write path and read-back) and
+sawkv_attn.hip (decode attention) into int4_kv_cache_amd/libsawkv.so.
 Flags: -ffp-contract=off (every float32 operation rounds on its own, as the
 bit-exact definition needs), no fast-math, denormals kept (the HIP default),
 and packed-fp32 instructions disabled.
@@ -14,7 +15,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "sawkv.hip")
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("sawkv.hip", "sawkv_attn.hip")]
 OUT = os.path.join(PKG, "libsawkv.so")
 ARCH = "gfx950"
 
@@ -38,7 +39,7 @@ def flags():
 
 def build(verbose=False):
     tmp = OUT + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + flags() + [SRC, "-o", tmp]
+    cmd = [hipcc()] + flags() + SRCS + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -22,6 +22,7 @@
 
 #include "sawkv.h"
 #include "sawkv_device.hpp"
+#include "sawkv_host.hpp"
 
 namespace sawkv {
 
@@ -461,7 +462,8 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherParams p) {
 // host side: validation, dispatch, C ABI
 // ---------------------------------------------------------------------------
 
-namespace {
+namespace sawkv {
+namespace host {
 
 thread_local char g_err[512];
 
@@ -479,6 +481,16 @@ int ok() {
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace host
+}  // namespace sawkv
+
+namespace {
+
+using sawkv::host::aligned;
+using sawkv::host::fail;
+using sawkv::host::g_err;
+using sawkv::host::ok;
 
 int check_geometry(int64_t T, int32_t H, int32_t D, int64_t N_pg, int32_t P, int32_t h,
                    int32_t rot_mode, const int64_t* slots) {

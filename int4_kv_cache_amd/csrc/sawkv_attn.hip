@@ -1,0 +1,776 @@
+// sawkv decode attention over the paged INT4 pools (gfx950, wave64).
+//
+// One decode step: every sequence b has one query token with Hq heads; query
+// head j reads KV head j / G (G = Hq / H). Keys and values are the INT4 rows
+// written by sawkv_quantize_append. The pages place dequantisation inside the
+// attention kernel (ainews.cool, "技术深度解析" item 3) and ask that the paged
+// layout and fused attention execution be kept (youngju.dev English page, "Why
+// the KV Cache Is the Real Bottleneck"); the rotation is orthogonal
+// (youngju.dev, "The Rotation Trick - Block-Diagonal Hadamard"), so for a
+// rotated key R^T y:  q . (R^T y) = (R q) . y.  The query is rotated once, and
+// no key is ever un-rotated; the value side is un-rotated once per output.
+//
+// Three kernels on the caller's stream, with a caller-provided workspace:
+//
+//  prep     one wave per (sequence, KV head): q' = R q (if keys are rotated),
+//           scaled by sm_scale * log2(e) and by a power of two 2^sigma that
+//           puts max |q'| in [2^13, 2^14); each value split into fp16
+//           hi + lo and laid out as the B operand of the score MFMAs.
+//  chunk    one wave per (sequence, chunk of C tokens, KV head): scores on
+//           the matrix cores straight from the packed nibbles, an online
+//           softmax, and P.V on the matrix cores; writes the chunk's partial
+//           (reference exponent, denominator, unnormalised output).
+//  combine  one quad per (sequence, query head): merges the chunks, divides,
+//           un-rotates V (if rotated), rounds to fp16.
+//
+// Nibbles on the matrix cores. A code byte holds two two's-complement
+// nibbles; xor 0x88 turns them into u = code + 8 in [0, 15]. Masking one
+// nibble into the low 10 bits of an fp16 lane gives the subnormal u * 2^-24
+// (bits 0-3) or 16u * 2^-24 (bits 4-7): exact values, no conversion
+// instruction. The MFMA multiplies subnormal fp16 inputs exactly. The factor
+// 16 on odd channels is folded into the other operand (1/16 on the query side,
+// a final 1/16 on the value side), and the +8 bias is removed by a per-query
+// constant: sum q' (u - 8) = sum q' u - 8 sum q'.
+//
+// Scores (16x16x32 f16 MFMA, 16 tokens x 16 columns x 32 channels): A =
+// codes (row m = token, one code dword per lane per MFMA), B = query
+// (column n < G: hi part of query n; G <= n < 2G: lo part; rest 0), so one
+// MFMA yields hi and lo dot products in two columns, added with one DPP
+// row shift. Lane (g = lane/16, n = lane%16) of the result holds tokens
+// 4g + j, j = 0..3, of column n.
+//
+// Values (16x16x32 MFMA, 16 rows x 16 columns x 32 tokens): A = weights
+// p * s_v (row n < G: hi part for query n; G <= n < 2G: lo part), taken
+// lane-locally from the score layout (k slot (g, i) is token 16(i/4) + 4g +
+// i%4 of the 32-token step); B = value nibbles: lane n loads code dword n
+// (channels 8n..8n+7) of its 8 tokens, and MFMA j uses nibble j, so column n
+// of MFMA j is channel 8n + j. Hi and lo rows are added once at the end.
+//
+// Softmax. Scores are kept in log2 units. The reference m tracks the largest
+// 4 * score + (bits of s_v >> 8), a cheap upper bound of 4 * log2(p * s_v)
+// + 60, so that every weight p * s_v stays below 2^14 in fp16; the reference
+// moves only when a new maximum exceeds it by 8 (in log2 units), so the
+// rescale of the accumulators is rare.
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "sawkv.h"
+#include "sawkv_device.hpp"
+#include "sawkv_host.hpp"
+
+namespace sawkv {
+namespace attn {
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kStep = 32;              // tokens per loop step (two 16-token tiles)
+constexpr int kQWords = 16;            // B-operand dwords per lane (4 MFMAs x 4)
+
+__device__ __forceinline__ f4_t mfma(u4_t a, u4_t b, f4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, a),
+                                                __builtin_bit_cast(h8_t, b), c, 0, 0, 0);
+}
+
+// Value of lane + S within the lane's row of 16 (0 past the row's end).
+template <int S>
+__device__ __forceinline__ float row_shl(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       0, __builtin_bit_cast(int, v), 0x100 + S, 0xF, 0xF, true));
+}
+
+// Lanes G..2G-1 of every row take `src` from lane - G; the others keep `old`.
+template <int G>
+__device__ __forceinline__ uint32_t lo_rows(uint32_t old, uint32_t src) {
+  constexpr int bank = G == 8 ? 0xC : G == 4 ? 0x2 : 0x1;
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, 0x110 + G, 0xF, bank, false);
+}
+
+// Row exchange on two copies of a value (rows = groups of 16 lanes):
+//   v_permlane16_swap a, b: a = [a0, b0, a2, b2], b = [a1, b1, a3, b3]
+//   v_permlane32_swap a, b: a = [a0, a1, b0, b1], b = [a2, a3, b2, b3]
+// With a = b = v, a op b combines rows (0,1)/(2,3) resp. (0,2)/(1,3). Written
+// as inline asm: the compiler folds the builtins' two results into one when
+// both inputs are the same value. The s_nop covers the VALU-write ->
+// permlane-read hazard (2 wait states), as for DPP.
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
+// Sum (or max) over the four rows of 16 lanes; every row gets the result.
+__device__ __forceinline__ float rows_sum(float v) {
+  float a = v, b = v;
+  swap16(a, b);
+  float c = a + b, d = a + b;
+  swap32(c, d);
+  return c + d;
+}
+
+__device__ __forceinline__ float rows_max(float v) {
+  float a = v, b = v;
+  swap16(a, b);
+  float c = fmaxf(a, b), d = fmaxf(a, b);
+  swap32(c, d);
+  return fmaxf(c, d);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+// ---------------------------------------------------------------------------
+// prep: q -> B operand of the score MFMAs
+// ---------------------------------------------------------------------------
+
+struct PrepParams {
+  const __half* q;
+  int64_t q_stride;        // elements between the rows of two sequences
+  uint32_t* qprep;         // [B][H][64][16]
+  float* qconst;           // [B][H][2][16]: C-init column values, log2 scale F
+  int32_t H;
+  int32_t h;
+  int32_t rot_k;
+  float c_h;               // f32(1/sqrt(h))
+  float c_sm;              // sm_scale * log2(e)
+};
+
+template <int G>
+__global__ __launch_bounds__(64) void attn_prep_kernel(PrepParams p) {
+  __shared__ float xs[G][kD];
+  const int lane = threadIdx.x;
+  const int64_t bh = blockIdx.x;
+  const int64_t b = bh / p.H;
+  const int h = (int)(bh % p.H);
+
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const __half* row = p.q + b * p.q_stride + (int64_t)(h * G + g) * kD;
+    xs[g][2 * lane] = __half2float(row[2 * lane]);
+    xs[g][2 * lane + 1] = __half2float(row[2 * lane + 1]);
+  }
+  __syncthreads();
+  if (p.rot_k) {
+    // Walsh-Hadamard butterflies within blocks of h channels; lane owns one
+    // pair (i, i + s) per query and stage.
+    for (int s = 1; s < p.h; s <<= 1) {
+      const int i = (lane / s) * 2 * s + (lane % s);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float a = xs[g][i], c = xs[g][i + s];
+        xs[g][i] = a + c;
+        xs[g][i + s] = a - c;
+      }
+      __syncthreads();
+    }
+  }
+  const float mul = p.rot_k ? p.c_h : 1.0f;
+
+  float sig_scale[G], cinit[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float v0 = xs[g][2 * lane] * mul * p.c_sm;
+    const float v1 = xs[g][2 * lane + 1] * mul * p.c_sm;
+    float amax = fmaxf(fabsf(v0), fabsf(v1));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    int e = 0;
+    if (amax > 0.0f) frexpf(amax, &e);            // amax in [2^(e-1), 2^e)
+    const int sigma = amax > 0.0f ? 14 - e : 0;   // max |Q| in [2^13, 2^14)
+    const float Q0 = ldexpf(v0, sigma), Q1 = ldexpf(v1, sigma);
+    // effective multiplier of u: (hi + lo) of Q (even channel) and of Q / 16
+    // times 16 (odd channel)
+    const _Float16 h0 = (_Float16)Q0;
+    const _Float16 l0 = (_Float16)(Q0 - (float)h0);
+    const float q16 = Q1 * 0.0625f;
+    const _Float16 h1 = (_Float16)q16;
+    const _Float16 l1 = (_Float16)(q16 - (float)h1);
+    float msum = ((float)h0 + (float)l0) + 16.0f * ((float)h1 + (float)l1);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) msum += __shfl_xor(msum, o);
+    cinit[g] = -8.0f * ldexpf(msum, -24);
+    sig_scale[g] = ldexpf(1.0f, 24 - sigma);
+    xs[g][2 * lane] = Q0;                      // each lane rewrites its own two channels
+    xs[g][2 * lane + 1] = q16;
+  }
+  __syncthreads();
+
+  const int gl = lane >> 4, n = lane & 15;
+  uint32_t words[kQWords];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ch0 = 8 * (4 * gl + c) + e, ch1 = ch0 + 4;
+      uint32_t w = 0;
+      if (n < 2 * G) {
+        const int qi = n < G ? n : n - G;
+        float v[2] = {xs[qi][ch0], xs[qi][ch1]};
+        uint16_t bits[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const _Float16 hi = (_Float16)v[k];
+          const _Float16 lo = (_Float16)(v[k] - (float)hi);
+          bits[k] = __builtin_bit_cast(uint16_t, n < G ? hi : lo);
+        }
+        w = (uint32_t)bits[0] | ((uint32_t)bits[1] << 16);
+      }
+      words[4 * c + e] = w;
+    }
+  }
+  u4_t* dst = reinterpret_cast<u4_t*>(p.qprep + (bh * 64 + lane) * kQWords);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    dst[k] = u4_t{words[4 * k], words[4 * k + 1], words[4 * k + 2], words[4 * k + 3]};
+  if (lane < 16) {
+    float ci = 0.0f, f = 0.0f;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      if (lane == g) { ci = cinit[g]; f = sig_scale[g]; }
+    p.qconst[bh * 32 + lane] = ci;
+    p.qconst[bh * 32 + 16 + lane] = f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// chunk: scores, online softmax, P.V over one chunk of one (sequence, head)
+// ---------------------------------------------------------------------------
+
+struct ChunkParams {
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const uint16_t* k_scales;
+  const uint16_t* v_scales;
+  const int32_t* block_tables;
+  int64_t bt_stride;
+  const int32_t* context_lens;
+  const uint32_t* qprep;
+  const float* qconst;
+  float* part_o;           // [B][NC][Hq][128]
+  float* part_ml;          // [B][NC][Hq][2]: reference exponent, denominator
+  int64_t N_pg;
+  int32_t P, H, Hq, NC, C, max_context;
+  uint32_t n_groups;       // B * NC
+};
+
+template <int G>
+__global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
+  const int lane = threadIdx.x;
+  const int g = lane >> 4, n = lane & 15;
+
+  // Block -> (sequence, chunk, head). Blocks are dealt to the 8 XCDs in turn
+  // (block i to XCD i % 8); the H heads of one (sequence, chunk) get
+  // consecutive blocks of one XCD, so the 64-byte rows of neighbouring heads,
+  // which share cache lines, meet in one L2.
+  const uint32_t bx = blockIdx.x;
+  const uint32_t r = bx >> 3;
+  const int h = (int)(r % (uint32_t)p.H);
+  const uint32_t grp = (r / (uint32_t)p.H) * 8u + (bx & 7u);
+  if (grp >= p.n_groups) return;
+  const int b = (int)(grp / (uint32_t)p.NC), c = (int)(grp % (uint32_t)p.NC);
+  int L = p.context_lens[b];
+  L = L < 0 ? 0 : (L > p.max_context ? p.max_context : L);
+  const int t_begin = c * p.C;
+  if (t_begin >= L) return;
+  const int t_end = min(t_begin + p.C, L);
+
+  const int64_t bh = (int64_t)b * p.H + h;
+  u4_t bq[4];
+  {
+    const u4_t* src = reinterpret_cast<const u4_t*>(p.qprep + (bh * 64 + lane) * kQWords);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) bq[k] = src[k];
+  }
+  const float cinit = p.qconst[bh * 32 + n];
+  const float F = p.qconst[bh * 32 + 16 + n];
+  const float F4 = 4.0f * F;
+
+  // lane offsets inside a 16-token tile (bytes for codes, elements for scales)
+  const int row_bytes = p.H * (kD / 2);
+  const int k_lane = n * row_bytes + 16 * g;
+  int v_lane[4], s_lane[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v_lane[j] = (4 * g + j) * row_bytes + 4 * n;
+    s_lane[j] = (4 * g + j) * p.H;
+  }
+
+  float m = -INFINITY, mref = 0.0f, l = 0.0f, W = 0.0f;
+  f4_t o[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o[k] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int32_t* bt = p.block_tables + (int64_t)b * p.bt_stride;
+
+  for (int t0 = t_begin; t0 < t_end; t0 += kStep) {
+    bool ok[2];
+    u4_t kq[2];
+    uint32_t vd[2][4], sk[2][4], sv[2][4];
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      const int st = t0 + 16 * T;
+      const int page = st < t_end ? bt[st / p.P] : -1;
+      ok[T] = page >= 0 && page < p.N_pg;
+      if (ok[T]) {
+        const int64_t slot0 = (int64_t)page * p.P + st % p.P;
+        const int64_t row0 = slot0 * p.H + h;
+        const uint8_t* kb = p.k_codes + row0 * (kD / 2);
+        const uint8_t* vb = p.v_codes + row0 * (kD / 2);
+        kq[T] = *reinterpret_cast<const u4_t*>(kb + k_lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          vd[T][j] = *reinterpret_cast<const uint32_t*>(vb + v_lane[j]);
+          sk[T][j] = p.k_scales[row0 + s_lane[j]];
+          sv[T][j] = p.v_scales[row0 + s_lane[j]];
+        }
+      } else {
+        kq[T] = u4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vd[T][j] = sk[T][j] = sv[T][j] = 0u;
+      }
+    }
+    const bool full = ok[0] && ok[1] && t0 + kStep <= t_end;
+
+    // scores: columns n < G hold hi, G <= n < 2G lo; add them with a row shift
+    float lam[2][4], mu[2][4];
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      f4_t acc = f4_t{cinit, cinit, cinit, cinit};
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const uint32_t w = kq[T][cc] ^ 0x88888888u;
+        const uint32_t w8 = w >> 8;
+        const u4_t a = u4_t{w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu,
+                            w8 & 0x00F000F0u};
+        acc = mfma(a, bq[cc], acc);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float s = acc[j] + row_shl<G>(acc[j]);
+        lam[T][j] = s * half_bits_to_float(sk[T][j]);
+        mu[T][j] = fmaf(F4, lam[T][j], (float)((sv[T][j] >> 8) & 0xFFu));
+      }
+    }
+    bool valid[2][4];
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        valid[T][j] = full || (ok[T] && t0 + 16 * T + 4 * g + j < t_end);
+        if (!valid[T][j]) mu[T][j] = -INFINITY;
+      }
+
+    float mx = fmaxf(fmaxf(fmaxf(mu[0][0], mu[0][1]), fmaxf(mu[0][2], mu[0][3])),
+                     fmaxf(fmaxf(mu[1][0], mu[1][1]), fmaxf(mu[1][2], mu[1][3])));
+    mx = rows_max(mx);
+    const bool need = n < G && mx > m + 32.0f;
+    if (__any(need)) {
+      const float mn = need ? mx : m;
+      const float alpha = need ? __builtin_amdgcn_exp2f((m - mn) * 0.25f) : 1.0f;
+      l *= alpha;
+      W *= alpha;
+      float al[G];
+#pragma unroll
+      for (int qc = 0; qc < G; ++qc)
+        al[qc] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                               __builtin_bit_cast(int, alpha), qc));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float a;
+        if constexpr (G == 8) a = (g & 1) ? al[4 + j] : al[j];
+        else a = al[j % G];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k][j] *= a;
+      }
+      m = mn;
+      mref = m * 0.25f - 20.0f;
+    }
+
+    // weights p * s_v, split into fp16 hi + lo for the A operand
+    float w[2][4];
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float pr = __builtin_amdgcn_exp2f(fmaf(F, lam[T][j], -mref));
+        float ww = pr * half_bits_to_float(sv[T][j]);
+        if (!valid[T][j]) pr = ww = 0.0f;
+        l += pr;
+        W += ww;
+        w[T][j] = ww;
+      }
+    u4_t A;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int T = e >> 1, j0 = 2 * (e & 1);
+      const h2_t hi = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(w[T][j0], w[T][j0 + 1]));
+      const h2_t lo = __builtin_bit_cast(
+          h2_t, __builtin_amdgcn_cvt_pkrtz(w[T][j0] - (float)hi[0], w[T][j0 + 1] - (float)hi[1]));
+      A[e] = lo_rows<G>(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo));
+    }
+
+    // values: lane n holds code dword n of tokens (T, j); MFMA j' uses nibble j'
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vd[T][j] ^= 0x88888888u;
+#pragma unroll
+    for (int beta = 0; beta < 4; ++beta) {
+      const uint32_t sel = (uint32_t)beta | (0x0Cu << 8) | ((4u + beta) << 16) | (0x0Cu << 24);
+      u4_t blo, bhi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int T = e >> 1, j0 = 2 * (e & 1);
+        const uint32_t x = __builtin_amdgcn_perm(vd[T][j0 + 1], vd[T][j0], sel);
+        blo[e] = x & 0x000F000Fu;
+        bhi[e] = x & 0x00F000F0u;
+      }
+      o[2 * beta] = mfma(A, blo, o[2 * beta]);
+      o[2 * beta + 1] = mfma(A, bhi, o[2 * beta + 1]);
+    }
+  }
+
+  // ---- chunk partial ----
+  l = rows_sum(l);
+  W = rows_sum(W);
+  f4_t os[8];
+  if constexpr (G == 4 || G == 8) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float a = o[k][j], b = o[k][j];
+        if constexpr (G == 4) swap16(a, b);
+        else swap32(a, b);
+        os[k][j] = a + b;
+      }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) os[k][j] = j < G ? o[k][j] + o[k][j + G] : 0.0f;
+  }
+  float Wq[G];
+#pragma unroll
+  for (int qc = 0; qc < G; ++qc)
+    Wq[qc] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, W), qc));
+
+  const int64_t head0 = (int64_t)grp * p.Hq + (int64_t)h * G;   // grp = b * NC + c
+  const bool writer = G == 8 ? g < 2 : g == 0;
+  if (writer) {
+#pragma unroll
+    for (int j = 0; j < (G < 4 ? G : 4); ++j) {
+      const int qi = G == 8 ? 4 * g + j : j;
+      float Wv;
+      if constexpr (G == 8) Wv = g ? Wq[4 + (j & 3)] : Wq[j & 3];
+      else Wv = Wq[j % G];
+      float vals[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        vals[k] = os[k][j] * ((k & 1) ? 1048576.0f : 16777216.0f) - 8.0f * Wv;
+      f4_t* dst = reinterpret_cast<f4_t*>(p.part_o + (head0 + qi) * kD + 8 * n);
+      dst[0] = f4_t{vals[0], vals[1], vals[2], vals[3]};
+      dst[1] = f4_t{vals[4], vals[5], vals[6], vals[7]};
+    }
+  }
+  if (g == 0 && n < G) {
+    p.part_ml[(head0 + n) * 2] = m == -INFINITY ? -INFINITY : mref;
+    p.part_ml[(head0 + n) * 2 + 1] = l;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// combine: merge chunks, normalise, un-rotate V, fp16
+// ---------------------------------------------------------------------------
+
+struct CombineParams {
+  const float* part_o;
+  const float* part_ml;
+  const int32_t* context_lens;
+  __half* out;             // [B][Hq][128]
+  int64_t n_vec;           // B * Hq
+  int32_t Hq, NC, C, max_context;
+};
+
+template <int HB>
+__global__ __launch_bounds__(64) void attn_combine_kernel(CombineParams p) {
+  const int lane = threadIdx.x, lam = lane & 3;
+  const int64_t v = (int64_t)blockIdx.x * 16 + (lane >> 2);
+  const bool live = v < p.n_vec;
+  const int64_t b = live ? v / p.Hq : 0;
+  const int qh = live ? (int)(v % p.Hq) : 0;
+  int L = live ? p.context_lens[b] : 0;
+  L = L < 0 ? 0 : (L > p.max_context ? p.max_context : L);
+  const int nck = (L + p.C - 1) / p.C;
+  const int64_t base = b * p.NC * p.Hq + qh;      // chunk c adds c * Hq
+
+  float M = -INFINITY;
+  for (int c = 0; c < nck; ++c) M = fmaxf(M, p.part_ml[(base + (int64_t)c * p.Hq) * 2]);
+
+  float x[kElems];
+#pragma unroll
+  for (int k = 0; k < kElems; ++k) x[k] = 0.0f;
+  float lsum = 0.0f;
+  if (M > -INFINITY) {
+    for (int c = 0; c < nck; ++c) {
+      const int64_t row = base + (int64_t)c * p.Hq;
+      const float ref = p.part_ml[row * 2];
+      if (ref == -INFINITY) continue;
+      const float sc = __builtin_amdgcn_exp2f(ref - M);
+      lsum += sc * p.part_ml[row * 2 + 1];
+      const f4_t* src = reinterpret_cast<const f4_t*>(p.part_o + row * kD + 8 * lam);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f4_t a = src[8 * i], bb = src[8 * i + 1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[8 * i + j] += sc * a[j];
+          x[8 * i + 4 + j] += sc * bb[j];
+        }
+      }
+    }
+  }
+  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+#pragma unroll
+  for (int k = 0; k < kElems; ++k) x[k] *= inv;
+  if constexpr (HB > 0) {
+    lane_stage<0>(x);
+    const float cs = fwht_rest<HB>(x, lam) * c_h<HB>();
+#pragma unroll
+    for (int k = 0; k < kElems; ++k) x[k] *= cs;
+  }
+  if (live) {
+    u4_t* dst = reinterpret_cast<u4_t*>(p.out + v * kD + 8 * lam);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t wd[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint16_t lo = __builtin_bit_cast(uint16_t, __float2half_rn(x[8 * i + 2 * k]));
+        const uint16_t hi = __builtin_bit_cast(uint16_t, __float2half_rn(x[8 * i + 2 * k + 1]));
+        wd[k] = (uint32_t)lo | ((uint32_t)hi << 16);
+      }
+      dst[4 * i] = u4_t{wd[0], wd[1], wd[2], wd[3]};
+    }
+  }
+}
+
+}  // namespace attn
+}  // namespace sawkv
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+namespace {
+
+using sawkv::host::aligned;
+using sawkv::host::fail;
+using sawkv::host::ok;
+
+constexpr int64_t kMaxContext = INT64_C(1) << 30;
+
+struct Layout {
+  int C;                   // tokens per chunk
+  int64_t NC;              // chunks per sequence
+  size_t qprep, qconst, ml, o, total;   // byte offsets and size
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Chunk length: 512 tokens, halved (down to 64) while the step would have
+// fewer than 8192 (sequence, chunk, head) items, so that small batches still
+// spread over every compute unit.
+Layout make_layout(int64_t B, int32_t Hq, int32_t H, int64_t max_context) {
+  Layout L{};
+  int C = 512;
+  while (C > 64 && B * H * ((max_context + C - 1) / C) < 8192) C >>= 1;
+  L.C = C;
+  L.NC = max_context > 0 ? (max_context + C - 1) / C : 1;
+  size_t off = 0;
+  L.qprep = off;
+  off = align256(off + (size_t)B * H * 64 * sawkv::attn::kQWords * 4);
+  L.qconst = off;
+  off = align256(off + (size_t)B * H * 32 * 4);
+  L.ml = off;
+  off = align256(off + (size_t)B * L.NC * Hq * 2 * 4);
+  L.o = off;
+  off = align256(off + (size_t)B * L.NC * Hq * sawkv::kD * 4);
+  L.total = off;
+  return L;
+}
+
+int check_attn_sizes(int64_t B, int32_t Hq, int32_t H, int32_t D, int64_t max_context) {
+  if (B < 0) return fail(SAWKV_EINVAL, "B = %lld is negative", (long long)B);
+  if (H <= 0 || Hq <= 0) return fail(SAWKV_EINVAL, "H = %d and Hq = %d must be positive", H, Hq);
+  if (Hq % H != 0) return fail(SAWKV_EINVAL, "Hq = %d is not a multiple of H = %d", Hq, H);
+  const int32_t G = Hq / H;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(SAWKV_EUNSUPPORTED, "Hq / H = %d unsupported (1, 2, 4 or 8)", G);
+  if (D != sawkv::kD) return fail(SAWKV_EUNSUPPORTED, "D = %d unsupported (only 128)", D);
+  if (H > 256) return fail(SAWKV_EUNSUPPORTED, "H = %d unsupported (at most 256)", H);
+  if (max_context < 0) return fail(SAWKV_EINVAL, "max_context = %lld is negative",
+                                   (long long)max_context);
+  if (max_context > kMaxContext)
+    return fail(SAWKV_EUNSUPPORTED, "max_context = %lld too large (at most 2^30)",
+                (long long)max_context);
+  if (B > (INT64_C(1) << 24))
+    return fail(SAWKV_EUNSUPPORTED, "B = %lld too large (at most 2^24)", (long long)B);
+  const Layout lay = make_layout(B, Hq, H, max_context);
+  // grid of the chunk kernel: ceil(B * NC / 8) * 8 * H blocks
+  if (((B * lay.NC + 7) / 8) * 8 * H >= (INT64_C(1) << 31))
+    return fail(SAWKV_EUNSUPPORTED, "B * chunks * H too large for one launch");
+  return SAWKV_OK;
+}
+
+using sawkv::attn::attn_chunk_kernel;
+using sawkv::attn::attn_combine_kernel;
+using sawkv::attn::attn_prep_kernel;
+
+int g_index(int32_t G) { return G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3; }
+
+const void* const kPrep[4] = {(void*)&attn_prep_kernel<1>, (void*)&attn_prep_kernel<2>,
+                              (void*)&attn_prep_kernel<4>, (void*)&attn_prep_kernel<8>};
+const void* const kChunk[4] = {(void*)&attn_chunk_kernel<1>, (void*)&attn_chunk_kernel<2>,
+                               (void*)&attn_chunk_kernel<4>, (void*)&attn_chunk_kernel<8>};
+const void* const kCombine[5] = {(void*)&attn_combine_kernel<0>, (void*)&attn_combine_kernel<16>,
+                                 (void*)&attn_combine_kernel<32>, (void*)&attn_combine_kernel<64>,
+                                 (void*)&attn_combine_kernel<128>};
+
+int launch64(const void* fn, int64_t blocks, void* params, hipStream_t stream) {
+  void* args[] = {params};
+  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(64), args, 0, stream);
+  if (e != hipSuccess) return fail(SAWKV_EHIP, "kernel launch: %s", hipGetErrorString(e));
+  return SAWKV_OK;
+}
+
+int attention_impl(const void* q, int64_t q_stride, const void* k_codes, const void* v_codes,
+                   const void* k_scales, const void* v_scales, int64_t N_pg, int32_t P,
+                   const int32_t* block_tables, int64_t bt_stride, const int32_t* context_lens,
+                   int64_t B, int32_t Hq, int32_t H, int32_t D, int64_t max_context,
+                   float sm_scale, int32_t h, int32_t rot_mode, void* out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  int st = check_attn_sizes(B, Hq, H, D, max_context);
+  if (st) return st;
+  if (P <= 0) return fail(SAWKV_EINVAL, "P = %d must be positive", P);
+  if (P % 16 != 0) return fail(SAWKV_EUNSUPPORTED, "P = %d unsupported (a multiple of 16)", P);
+  if (N_pg <= 0) return fail(SAWKV_EINVAL, "N_pg = %lld must be positive", (long long)N_pg);
+  if (N_pg > INT32_MAX)
+    return fail(SAWKV_EUNSUPPORTED, "N_pg = %lld too large (page ids are int32)", (long long)N_pg);
+  if (N_pg * P > (INT64_C(1) << 56) / ((int64_t)H * D))
+    return fail(SAWKV_EINVAL, "pool of %lld pages x %d slots is too large", (long long)N_pg, P);
+  if (h != 16 && h != 32 && h != 64 && h != 128)
+    return fail(SAWKV_EUNSUPPORTED, "h = %d unsupported (16, 32, 64 or 128)", h);
+  if (rot_mode != SAWKV_ROT_NONE && rot_mode != SAWKV_ROT_K && rot_mode != SAWKV_ROT_KV)
+    return fail(SAWKV_EINVAL, "rot_mode = %d invalid", rot_mode);
+  if (!(fabsf(sm_scale) <= 3.0e38f)) return fail(SAWKV_EINVAL, "sm_scale is not finite");
+  if (bt_stride < (max_context + P - 1) / P)
+    return fail(SAWKV_EINVAL, "bt_stride %lld < ceil(max_context / P) = %lld",
+                (long long)bt_stride, (long long)((max_context + P - 1) / P));
+  if (q_stride < (int64_t)Hq * D)
+    return fail(SAWKV_EINVAL, "q_stride %lld < Hq*D = %d", (long long)q_stride, Hq * D);
+  if (q_stride % 8 != 0)
+    return fail(SAWKV_EALIGN, "q_stride %lld not a multiple of 8", (long long)q_stride);
+  if (B == 0) return ok();
+  if (!q || !k_codes || !v_codes || !k_scales || !v_scales || !block_tables || !context_lens ||
+      !out || !workspace)
+    return fail(SAWKV_EINVAL, "a tensor or workspace pointer is NULL");
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
+      !aligned(k_scales, 16) || !aligned(v_scales, 16) || !aligned(workspace, 256))
+    return fail(SAWKV_EALIGN, "q, out and pools must be 16-byte aligned, workspace 256-byte");
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return fail(SAWKV_EALIGN, "block_tables / context_lens not 4-byte aligned");
+  const Layout lay = make_layout(B, Hq, H, max_context);
+  if (workspace_bytes < lay.total)
+    return fail(SAWKV_EINVAL, "workspace of %zu bytes < %zu needed", workspace_bytes, lay.total);
+
+  const int32_t G = Hq / H;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  sawkv::attn::PrepParams pp{};
+  pp.q = static_cast<const __half*>(q);
+  pp.q_stride = q_stride;
+  pp.qprep = reinterpret_cast<uint32_t*>(ws + lay.qprep);
+  pp.qconst = reinterpret_cast<float*>(ws + lay.qconst);
+  pp.H = H;
+  pp.h = h;
+  pp.rot_k = rot_mode != SAWKV_ROT_NONE;
+  pp.c_h = (float)(1.0 / sqrt((double)h));
+  pp.c_sm = (float)((double)sm_scale * 1.4426950408889634);
+  if ((st = launch64(kPrep[g_index(G)], B * H, &pp, s))) return st;
+
+  sawkv::attn::ChunkParams cp{};
+  cp.k_codes = static_cast<const uint8_t*>(k_codes);
+  cp.v_codes = static_cast<const uint8_t*>(v_codes);
+  cp.k_scales = static_cast<const uint16_t*>(k_scales);
+  cp.v_scales = static_cast<const uint16_t*>(v_scales);
+  cp.block_tables = block_tables;
+  cp.bt_stride = bt_stride;
+  cp.context_lens = context_lens;
+  cp.qprep = pp.qprep;
+  cp.qconst = pp.qconst;
+  cp.part_o = reinterpret_cast<float*>(ws + lay.o);
+  cp.part_ml = reinterpret_cast<float*>(ws + lay.ml);
+  cp.N_pg = N_pg;
+  cp.P = P;
+  cp.H = H;
+  cp.Hq = Hq;
+  cp.NC = (int32_t)lay.NC;
+  cp.C = lay.C;
+  cp.max_context = (int32_t)max_context;
+  cp.n_groups = (uint32_t)(B * lay.NC);
+  const int64_t chunk_blocks = ((B * lay.NC + 7) / 8) * 8 * H;
+  if (max_context > 0 && (st = launch64(kChunk[g_index(G)], chunk_blocks, &cp, s))) return st;
+
+  sawkv::attn::CombineParams mp{};
+  mp.part_o = cp.part_o;
+  mp.part_ml = cp.part_ml;
+  mp.context_lens = context_lens;
+  mp.out = static_cast<__half*>(out);
+  mp.n_vec = B * Hq;
+  mp.Hq = Hq;
+  mp.NC = cp.NC;
+  mp.C = lay.C;
+  mp.max_context = (int32_t)max_context;
+  const int hv = rot_mode == SAWKV_ROT_KV ? (h == 16 ? 1 : h == 32 ? 2 : h == 64 ? 3 : 4) : 0;
+  if ((st = launch64(kCombine[hv], (B * Hq + 15) / 16, &mp, s))) return st;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int sawkv_decode_attention_workspace_size(int64_t B, int32_t Hq, int32_t H, int32_t D,
+                                          int64_t max_context, size_t* bytes) {
+  if (bytes == nullptr) return fail(SAWKV_EINVAL, "bytes is NULL");
+  const int st = check_attn_sizes(B, Hq, H, D, max_context);
+  if (st) return st;
+  *bytes = make_layout(B, Hq, H, max_context).total;
+  return ok();
+}
+
+int sawkv_decode_attention(const void* q, int64_t q_stride, const void* k_codes,
+                           const void* v_codes, const void* k_scales, const void* v_scales,
+                           int64_t N_pg, int32_t P, const int32_t* block_tables,
+                           int64_t bt_stride, const int32_t* context_lens, int64_t B,
+                           int32_t Hq, int32_t H, int32_t D, int64_t max_context,
+                           float sm_scale, int32_t h, int32_t rot_mode, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_impl(q, q_stride, k_codes, v_codes, k_scales, v_scales, N_pg, P,
+                        block_tables, bt_stride, context_lens, B, Hq, H, D, max_context,
+                        sm_scale, h, rot_mode, out, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

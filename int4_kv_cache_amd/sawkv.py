@@ -50,6 +50,13 @@ lib.sawkv_naive_int4_append.restype = ctypes.c_int
 lib.sawkv_naive_int4_gather.argtypes = [_p, _p, _p, _p, _i64, _i32, _p, _i64, _i32, _i32,
                                         _p, _p, _p]
 lib.sawkv_naive_int4_gather.restype = ctypes.c_int
+lib.sawkv_decode_attention_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i64,
+                                                      ctypes.POINTER(ctypes.c_size_t)]
+lib.sawkv_decode_attention_workspace_size.restype = ctypes.c_int
+lib.sawkv_decode_attention.argtypes = [_p, _i64, _p, _p, _p, _p, _i64, _i32, _p, _i64, _p,
+                                       _i64, _i32, _i32, _i32, _i64, ctypes.c_float, _i32, _i32,
+                                       _p, _p, ctypes.c_size_t, _p]
+lib.sawkv_decode_attention.restype = ctypes.c_int
 lib.sawkv_status_string.argtypes = [ctypes.c_int]
 lib.sawkv_status_string.restype = ctypes.c_char_p
 lib.sawkv_last_error.argtypes = []
@@ -256,3 +263,71 @@ def naive_int4_gather(k_codes, v_codes, k_scales, v_scales, slot_mapping, *, k_o
         _addr(k_scales) if want_k else None, _addr(v_scales) if want_v else None,
         N_pg, P, _addr(slot_mapping), T, H, D, _addr(k_out), _addr(v_out), _stream(stream)))
     return k_out, v_out
+
+
+def attention_workspace_size(B, Hq, H, max_context, D=128):
+    """Bytes of workspace sawkv_decode_attention needs for these sizes."""
+    n = ctypes.c_size_t(0)
+    _check(lib.sawkv_decode_attention_workspace_size(B, Hq, H, D, max_context, ctypes.byref(n)))
+    return n.value
+
+
+def _attention_args(q, pools, block_tables, context_lens, max_context, h, rot, sm_scale, out,
+                    workspace):
+    k_codes, v_codes, k_scales, v_scales = pools
+    N_pg, P, H, half = _pool_geometry(k_codes, k_scales)
+    if tuple(_pool_geometry(v_codes, v_scales)) != (N_pg, P, H, half):
+        raise ValueError("K and V pools must have the same shape")
+    D = 2 * half
+    if q.dtype != torch.float16 or q.dim() != 3 or q.shape[2] != D or q.stride(2) != 1 \
+            or (q.shape[1] > 1 and q.stride(1) != D):
+        raise ValueError("q must be fp16 [B, Hq, D] with unit channel stride and head stride D")
+    B, Hq = q.shape[0], q.shape[1]
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 \
+            or block_tables.shape[0] != B or block_tables.stride(1) != 1:
+        raise ValueError("block_tables must be int32 [B, max_pages] with unit column stride")
+    if context_lens.dtype != torch.int32 or context_lens.numel() != B \
+            or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be contiguous int32 [B]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
+    if out.dtype != torch.float16 or tuple(out.shape) != (B, Hq, D) or not out.is_contiguous():
+        raise ValueError("out must be contiguous fp16 [B, Hq, D]")
+    need = attention_workspace_size(B, Hq, H, max_context, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if sm_scale is None:
+        sm_scale = 1.0 / float(D) ** 0.5
+    bt_stride = block_tables.stride(0) if B > 0 else block_tables.shape[1]
+    return (_addr(q), q.stride(0) if B > 0 else Hq * D, _addr(k_codes), _addr(v_codes),
+            _addr(k_scales), _addr(v_scales), N_pg, P, _addr(block_tables), bt_stride,
+            _addr(context_lens), B, Hq, H, D, max_context, float(sm_scale), h, _rot(rot),
+            _addr(out), _addr(workspace), workspace.numel() * workspace.element_size()), \
+        out, workspace
+
+
+def decode_attention(q, pools, block_tables, context_lens, max_context, *, h=128, rot="k",
+                     sm_scale=None, out=None, workspace=None, stream=None):
+    """One decode step of attention over the paged INT4 pools
+    (sawkv_decode_attention). pools = (k_codes, v_codes, k_scales, v_scales).
+    Returns out, fp16 [B, Hq, D]."""
+    args, out, _ = _attention_args(q, pools, block_tables, context_lens, max_context, h, rot,
+                                   sm_scale, out, workspace)
+    _check(lib.sawkv_decode_attention(*args, _stream(stream)))
+    return out
+
+
+class AttentionCall:
+    """sawkv_decode_attention with arguments checked and marshalled once (and
+    the workspace allocated once); calling the object only launches. The
+    tensors must stay alive and keep their storage while the object is used."""
+
+    def __init__(self, q, pools, block_tables, context_lens, max_context, *, h=128, rot="k",
+                 sm_scale=None, out=None, workspace=None):
+        self._args, self.out, self.workspace = _attention_args(
+            q, pools, block_tables, context_lens, max_context, h, rot, sm_scale, out, workspace)
+        self._keep = (q, pools, block_tables, context_lens)
+
+    def __call__(self, stream=None):
+        _check(lib.sawkv_decode_attention(*self._args, _stream(stream)))
+        return self.out

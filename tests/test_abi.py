@@ -188,3 +188,93 @@ def test_layers_validation(lib):
     assert layers_call(lib, nul) == EINVAL
     assert layers_call(lib, descs, h=40) == EUNSUPPORTED
     assert layers_call(lib, descs, T=0) == OK                          # nothing launched
+
+
+# ---- decode attention: every call below stops in validation (the base case
+# has a 1-byte workspace, which is the last check) or has B == 0 ----
+
+Q, BT, CL, OUT, WS = (A * i for i in range(8, 13))
+
+
+def attn(lib, **kw):
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.sawkv_decode_attention.argtypes = [p, i64, p, p, p, p, i64, i32, p, i64, p, i64, i32,
+                                           i32, i32, i64, ctypes.c_float, i32, i32, p, p,
+                                           ctypes.c_size_t, p]
+    a = dict(q=Q, qs=32 * 128, kc=KC, vc=VC, kss=KS, vss=VS, npg=64, P=16, bt=BT, bts=64,
+             cl=CL, B=4, Hq=32, H=8, D=128, maxc=1000, sm=0.088, h=128, rot=1, out=OUT, ws=WS,
+             wsb=1)
+    a.update(kw)
+    return lib.sawkv_decode_attention(a["q"], a["qs"], a["kc"], a["vc"], a["kss"], a["vss"],
+                                      a["npg"], a["P"], a["bt"], a["bts"], a["cl"], a["B"],
+                                      a["Hq"], a["H"], a["D"], a["maxc"], a["sm"], a["h"],
+                                      a["rot"], a["out"], a["ws"], a["wsb"], None)
+
+
+def attn_ws(lib, B=4, Hq=32, H=8, D=128, maxc=1000):
+    lib.sawkv_decode_attention_workspace_size.argtypes = [
+        ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+        ctypes.POINTER(ctypes.c_size_t)]
+    n = ctypes.c_size_t(0)
+    st = lib.sawkv_decode_attention_workspace_size(B, Hq, H, D, maxc, ctypes.byref(n))
+    return st, n.value
+
+
+def test_attention_base_case_stops_at_workspace_size(lib):
+    assert attn(lib) == EINVAL
+    assert b"workspace" in lib.sawkv_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), EINVAL),
+    (dict(H=0), EINVAL),
+    (dict(Hq=30), EINVAL),
+    (dict(Hq=24), EUNSUPPORTED),
+    (dict(Hq=128), EUNSUPPORTED),
+    (dict(D=64, qs=32 * 64), EUNSUPPORTED),
+    (dict(H=512, Hq=512, qs=512 * 128), EUNSUPPORTED),
+    (dict(maxc=-1), EINVAL),
+    (dict(maxc=(1 << 30) + 1, bts=1 << 27), EUNSUPPORTED),
+    (dict(P=0), EINVAL),
+    (dict(P=8), EUNSUPPORTED),
+    (dict(P=24), EUNSUPPORTED),
+    (dict(npg=0), EINVAL),
+    (dict(npg=1 << 31), EUNSUPPORTED),
+    (dict(h=8), EUNSUPPORTED),
+    (dict(rot=3), EINVAL),
+    (dict(sm=float("inf")), EINVAL),
+    (dict(sm=float("nan")), EINVAL),
+    (dict(bts=62), EINVAL),
+    (dict(qs=32 * 128 - 8), EINVAL),
+    (dict(qs=32 * 128 + 4), EALIGN),
+    (dict(q=None), EINVAL),
+    (dict(bt=None), EINVAL),
+    (dict(cl=None), EINVAL),
+    (dict(out=None), EINVAL),
+    (dict(ws=None), EINVAL),
+    (dict(q=Q + 8), EALIGN),
+    (dict(vss=VS + 2), EALIGN),
+    (dict(ws=WS + 16), EALIGN),
+    (dict(bt=BT + 2), EALIGN),
+])
+def test_attention_validation(lib, kw, status):
+    assert attn(lib, **kw) == status
+    assert lib.sawkv_last_error() != b""
+
+
+def test_attention_empty_batch_reads_nothing(lib):
+    assert attn(lib, B=0, q=None, kc=None, vc=None, kss=None, vss=None, bt=None, cl=None,
+                out=None, ws=None, wsb=0) == OK
+
+
+def test_attention_workspace_size(lib):
+    st, n = attn_ws(lib)
+    assert st == OK and n > 0 and n % 256 == 0
+    # grows with the batch and the context; rejects what the call rejects
+    assert attn_ws(lib, B=8)[1] > n
+    assert attn_ws(lib, maxc=100000)[1] > n
+    assert attn_ws(lib, Hq=24)[0] == EUNSUPPORTED
+    assert attn_ws(lib, maxc=-3)[0] == EINVAL
+    # a workspace one byte short of the reported size is refused
+    assert attn(lib, wsb=n - 1) == EINVAL
+    assert b"workspace" in lib.sawkv_last_error()

@@ -1,0 +1,265 @@
+"""GPU parity of decode attention over the paged INT4 pools (sawkv_decode_attention,
+called through the C ABI) against the float64 oracle.
+
+Tolerance, per output element of sequence b and query head j (derived from the
+kernel's arithmetic; Vmax bounds |V_t| over the context, Bmax bounds the
+log2-unit logits' L1 magnitude):
+
+    |got - ref| <= 2^-10 |ref| + Vmax * (2^-14 + 2^-17 * Bmax)
+
+  * 2^-10 |ref|: the final fp16 rounding (half an ulp is <= 2^-11 |ref|).
+  * Vmax * 2^-14: the value side. The weights p * s_v enter the matrix cores as
+    fp16 hi + lo (relative error <= 2^-22), products with the codes are exact,
+    float32 accumulation rounds once per 32 tokens, and the +8 code bias is
+    removed with a float32 running sum (<= 2^-17 relative over a chunk, times
+    8).
+  * Vmax * 2^-17 * Bmax: the logits. The query enters as fp16 hi + lo
+    (<= 2^-22 relative per channel); the bias constant and five float32
+    roundings of sums bounded by 23 * sum |q'| * 8 give an absolute logit
+    error below 2^-19 * Bmax (log2 units), and a logit error d moves the
+    softmax average by at most 2 ln 2 * d * Vmax.
+  Bmax = sm_scale * log2(e) * max_t s_k,t * 8 * ||R q||_1 (R the rotation
+  when keys are rotated); Vmax = 8 * max_t s_v,t, times sqrt(h) when values
+  are rotated (an error in the rotated basis grows by at most sqrt(h) in one
+  channel after the inverse rotation).
+"""
+import dataclasses
+import math
+import sys
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+from oracle import sawint4 as O
+from int4_kv_cache_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+ROTS = {O.ROT_NONE: "none", O.ROT_K: "k", O.ROT_KV: "kv"}
+LOG2E = 1.4426950408889634
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm device")
+    from int4_kv_cache_amd import sawkv as S   # raises if libsawkv.so is missing
+    return torch, S
+
+
+def say(*a):
+    print("[gpu]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(env, x):
+    torch, _ = env
+    return {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in x.items()}
+
+
+def run_gpu(env, x, max_context, h, rot, sm_scale=None, q=None):
+    torch, S = env
+    d = to_dev(env, x)
+    pools = (d["k_codes"], d["v_codes"], d["k_scales"], d["v_scales"])
+    out = S.decode_attention(d["q"] if q is None else q, pools, d["block_tables"],
+                             d["context_lens"], max_context, h=h, rot=ROTS[rot],
+                             sm_scale=sm_scale)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def run_oracle(x, h, rot, seqs=None, sm_scale=None, max_context=None):
+    L = np.asarray(x["context_lens"]).astype(np.int64)
+    if max_context is not None:
+        L = np.clip(L, 0, max_context)
+    seqs = np.arange(len(L)) if seqs is None else np.asarray(seqs)
+    return O.paged_decode_attention(x["q"][seqs], x["k_codes"], x["k_scales"], x["v_codes"],
+                                    x["v_scales"], x["block_tables"][seqs], L[seqs], h=h,
+                                    rot_mode=rot, sm_scale=sm_scale)
+
+
+def tolerance(x, h, rot, seqs, ref, sm_scale=None, max_context=None):
+    """Per-element bound from the module docstring."""
+    q = x["q"][seqs].astype(np.float64)
+    B, Hq, D = q.shape
+    n_pg, P, H, _ = x["k_codes"].shape
+    G = Hq // H
+    sm = 1.0 / math.sqrt(D) if sm_scale is None else sm_scale
+    if rot != O.ROT_NONE:
+        blk = np.kron(np.eye(D // h), scipy.linalg.hadamard(h) / math.sqrt(h))
+        q = q @ blk.T
+    l1 = np.abs(q).sum(-1)                                     # [B, Hq]
+    tol = np.zeros_like(ref)
+    ks = x["k_scales"].reshape(n_pg * P, H).astype(np.float64)
+    vs = x["v_scales"].reshape(n_pg * P, H).astype(np.float64)
+    vfac = 8.0 * (math.sqrt(h) if rot == O.ROT_KV else 1.0)
+    for i, b in enumerate(seqs):
+        L = int(x["context_lens"][b])
+        if max_context is not None:
+            L = min(max(L, 0), max_context)
+        t = np.arange(L)
+        pages = x["block_tables"][b][t // P].astype(np.int64)
+        ok = (pages >= 0) & (pages < n_pg)
+        slots = (pages * P + t % P)[ok]
+        if len(slots) == 0:
+            continue
+        for j in range(Hq):
+            kv = j // G
+            bmax = abs(sm) * LOG2E * ks[slots, kv].max() * 8.0 * l1[i, j]
+            vmax = vfac * vs[slots, kv].max()
+            tol[i, j] = vmax * (2.0 ** -14 + 2.0 ** -17 * bmax)
+    return 2.0 ** -10 * np.abs(ref) + tol
+
+
+def check(got, ref, tol, what):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.abs(got.astype(np.float64) - ref)
+    ratio = err / np.maximum(tol, 1e-300)
+    worst = np.unravel_index(np.argmax(ratio), ratio.shape)
+    say(f"{what}: max err {err.max():.3g}, max err/tol {ratio.max():.3g} at {worst}, "
+        f"median |ref| {np.median(np.abs(ref)):.3g}")
+    assert ratio.max() <= 1.0, f"{what}: error {err[worst]:.4g} > tol {tol[worst]:.4g} at {worst}"
+
+
+def small(**kw):
+    return dataclasses.replace(W.ATTN_WORKLOADS["attn_small"], **kw)
+
+
+# --------------------------------------------------------------------------
+# small cases: every output element against the oracle
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rot", [O.ROT_NONE, O.ROT_K, O.ROT_KV])
+@pytest.mark.parametrize("h", [16, 32, 64, 128])
+def test_small_all_rotations(env, rot, h):
+    wl = small(h=h, rot_mode=rot)
+    x = W.attn_inputs(wl)
+    maxc = int(x["context_lens"].max())
+    say(f"attn_small rot={ROTS[rot]} h={h} L={x['context_lens'].tolist()}")
+    got = run_gpu(env, x, maxc, h, rot)
+    ref = run_oracle(x, h, rot)
+    check(got, ref, tolerance(x, h, rot, np.arange(wl.B), ref), f"small rot={rot} h={h}")
+    assert np.array_equal(got[0], np.zeros_like(got[0]))          # empty context
+
+
+@pytest.mark.parametrize("Hq,H", [(8, 8), (16, 8), (64, 8), (4, 1), (2, 2)])
+def test_group_sizes(env, Hq, H):
+    wl = small(Hq=Hq, H=H, wid=8 + Hq + H)
+    x = W.attn_inputs(wl)
+    say(f"attn G={Hq // H} Hq={Hq} H={H}")
+    got = run_gpu(env, x, int(x["context_lens"].max()), 128, O.ROT_KV)
+    ref = run_oracle(x, 128, O.ROT_KV)
+    check(got, ref, tolerance(x, 128, O.ROT_KV, np.arange(wl.B), ref), f"G={Hq // H}")
+
+
+@pytest.mark.parametrize("P", [32, 64])
+def test_page_sizes(env, P):
+    wl = small(P=P, wid=20 + P)
+    x = W.attn_inputs(wl)
+    say(f"attn P={P}")
+    got = run_gpu(env, x, int(x["context_lens"].max()), 128, O.ROT_K)
+    ref = run_oracle(x, 128, O.ROT_K)
+    check(got, ref, tolerance(x, 128, O.ROT_K, np.arange(wl.B), ref), f"P={P}")
+
+
+def test_lengths_beyond_max_context_and_negative(env):
+    x = W.attn_inputs(small())
+    x["context_lens"] = np.array([0, 1, 15, -5, 17, 33, 100, 700, 1300], dtype=np.int32)
+    maxc = 650
+    say("attn lengths clipped to max_context=650, one negative")
+    got = run_gpu(env, x, maxc, 128, O.ROT_KV)
+    ref = run_oracle(x, 128, O.ROT_KV, max_context=maxc)
+    check(got, ref, tolerance(x, 128, O.ROT_KV, np.arange(9), ref, max_context=maxc), "clip")
+    assert np.array_equal(got[3], np.zeros_like(got[3]))
+
+
+def test_zero_max_context_gives_zeros(env):
+    x = W.attn_inputs(small())
+    say("attn max_context=0")
+    got = run_gpu(env, x, 0, 128, O.ROT_KV)
+    assert np.array_equal(got, np.zeros_like(got))
+
+
+def test_strided_q_and_custom_scale(env):
+    torch, S = env
+    x = W.attn_inputs(small())
+    big = torch.zeros((9, 48, 128), dtype=torch.float16, device="cuda")
+    big[:, 5:37] = torch.from_numpy(x["q"]).cuda()
+    q = big[:, 5:37]                                       # row stride 48*128
+    for sm in (0.05, -0.2):
+        say(f"attn strided q, sm_scale={sm}")
+        got = run_gpu(env, x, 1300, 64, O.ROT_KV, sm_scale=sm, q=q)
+        ref = run_oracle(x, 64, O.ROT_KV, sm_scale=sm)
+        check(got, ref, tolerance(x, 64, O.ROT_KV, np.arange(9), ref, sm_scale=sm),
+              f"sm={sm}")
+
+
+def test_peaked_softmax_outlier_heads(env):
+    """Scales 20x larger on two heads per tensor make the softmax nearly
+    one-hot there; sharpen further with a large sm_scale."""
+    x = W.attn_inputs(small())
+    say("attn sm_scale=1.0 (peaked)")
+    got = run_gpu(env, x, 1300, 128, O.ROT_K, sm_scale=1.0)
+    ref = run_oracle(x, 128, O.ROT_K, sm_scale=1.0)
+    check(got, ref, tolerance(x, 128, O.ROT_K, np.arange(9), ref, sm_scale=1.0), "peaked")
+
+
+# --------------------------------------------------------------------------
+# end to end: the product write path fills the pool, attention reads it
+# --------------------------------------------------------------------------
+
+def test_append_then_attention(env):
+    """K/V of the sweep recipe written by sawkv_quantize_append on the GPU and
+    by the oracle on the CPU; the pools must agree byte for byte, and the
+    attention over them must match the oracle's attention over its own pool."""
+    torch, S = env
+    wl = dataclasses.replace(W.WORKLOADS["sweep"], n_seq=4, seq_len=700, N_pg=4096)
+    k, v = W.kv(wl)
+    slots = W.slot_mapping(wl)
+    for rot in (O.ROT_K, O.ROT_KV):
+        say(f"append then attention rot={ROTS[rot]}")
+        kc, vc, ks, vs = S.alloc_pools(wl.N_pg, wl.P, wl.H, wl.D, "cuda", code_fill=0,
+                                       scale_bits_fill=0)
+        S.quantize_append(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                          torch.from_numpy(slots).cuda(), kc, vc, ks, vs, h=128, rot=ROTS[rot])
+        okc = np.zeros((wl.N_pg, wl.P, wl.H, wl.D // 2), np.uint8)
+        ovc = okc.copy()
+        oks = np.zeros((wl.N_pg, wl.P, wl.H), np.float16)
+        ovs = oks.copy()
+        O.quantize_append(k, v, slots, okc, ovc, oks, ovs, 128, rot)
+        assert kc.cpu().numpy().tobytes() == okc.tobytes()
+        assert vs.cpu().numpy().tobytes() == ovs.tobytes()
+        # pages of sequence s are the free-list pages its tokens were written to
+        pages = (slots // wl.P).reshape(wl.n_seq, wl.seq_len)[:, ::wl.P].astype(np.int32)
+        L = np.array([700, 1, 350, 699], dtype=np.int32)
+        rng = np.random.default_rng(5)
+        q = rng.standard_normal((wl.n_seq, 4 * wl.H, wl.D)).astype(np.float16)
+        x = {"q": q, "k_codes": okc, "v_codes": ovc, "k_scales": oks, "v_scales": ovs,
+             "block_tables": pages, "context_lens": L}
+        got = S.decode_attention(torch.from_numpy(q).cuda(), (kc, vc, ks, vs),
+                                 torch.from_numpy(pages).cuda(), torch.from_numpy(L).cuda(), 700,
+                                 h=128, rot=ROTS[rot])
+        torch.cuda.synchronize()
+        got = got.cpu().numpy()
+        ref = run_oracle(x, 128, rot)
+        check(got, ref, tolerance(x, 128, rot, np.arange(4), ref), f"e2e rot={rot}")
+
+
+# --------------------------------------------------------------------------
+# full size: 256 sequences, contexts up to 8000, sampled against the oracle
+# --------------------------------------------------------------------------
+
+def test_full_size_sampled(env):
+    wl = W.ATTN_WORKLOADS["attn"]
+    x = W.attn_inputs(wl)
+    L = x["context_lens"]
+    maxc = int(L.max())
+    say(f"attn full size B={wl.B} tokens={int(L.sum())} max={maxc}")
+    got = run_gpu(env, x, maxc, wl.h, wl.rot_mode)
+    rng = np.random.default_rng(0)
+    seqs = np.unique(np.r_[np.argmin(L), np.argmax(L), rng.choice(wl.B, 4, replace=False)])
+    ref = run_oracle(x, wl.h, wl.rot_mode, seqs=seqs)
+    check(got[seqs], ref, tolerance(x, wl.h, wl.rot_mode, seqs, ref), "full sampled")
+    assert np.all(np.isfinite(got))
