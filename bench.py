@@ -1,6 +1,7 @@
 """Benchmark of the fused Hadamard + INT4 paged append (sawkv) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
+    python bench.py --workload attn     (decode attention over the INT4 pool)
 
 One step = one sawkv_quantize_append call over the workload's batch (rotate,
 token-wise INT4, pack, scatter into the paged pool: the whole write path).
@@ -12,6 +13,11 @@ Prints ONE JSON line. Alongside the step it times, on the same batch:
   * the CPU oracle on a bounded sample of the same batch (a baseline only).
 Roofline: achieved HBM GB/s of the append kernel (algorithmic bytes per launch
 over the event-timed average launch) against the MI355X HBM3E peak, 8 TB/s.
+
+With --workload attn one step is one sawkv_decode_attention call (query prep,
+chunk kernel, combine) over 256 sequences whose contexts already sit in the
+INT4 pool; its bytes are the K and V codes and scales of every context token,
+the queries, the outputs and the block tables.
 """
 import argparse
 import hashlib
@@ -33,17 +39,21 @@ HBM_PEAK_GBPS = 8000.0
 ROT_NAME = {0: "none", 1: "k", 2: "kv"}
 KERNEL_SRC = [os.path.join(ROOT, "int4_kv_cache_amd", "csrc", f)
               for f in ("sawkv.hip", "sawkv_device.hpp")]
+ATTN_SRC = [os.path.join(ROOT, "int4_kv_cache_amd", "csrc", f)
+            for f in ("sawkv_attn.hip", "sawkv_device.hpp")]
+ATTN_METRIC = ("GB/s and decode tokens/s of attention over the paged INT4 KV cache "
+               "(fused dequant); % HBM peak; vs naive INT4")
 
 
-def kernel_source_hash():
+def kernel_source_hash(srcs=KERNEL_SRC):
     h = hashlib.sha256()
-    for p in KERNEL_SRC:
+    for p in srcs:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, srcs=KERNEL_SRC):
     """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
     taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -53,7 +63,7 @@ def measured_traffic(workload):
     except (OSError, ValueError):
         return None
     ent = rec.get(workload)
-    if not ent or ent.get("kernel_source_hash") != kernel_source_hash():
+    if not ent or ent.get("kernel_source_hash") != kernel_source_hash(srcs):
         return None
     return ent.get("bytes_per_launch")
 
@@ -143,12 +153,143 @@ def decode_extras(torch, step_rot, timed, stream, wl, layers):
             "graph_tokens_per_s": round(wl.T / (graph_ms * 1e-3), 1)}
 
 
+def attn_bytes(wl, x):
+    """Algorithmic HBM bytes of one decode-attention step: K and V codes and
+    scales of every context token, block-table entries, context lengths,
+    queries in and outputs out."""
+    L = x["context_lens"].astype(np.int64)
+    pages = (L + wl.P - 1) // wl.P
+    return int(L.sum() * wl.bytes_per_token() + pages.sum() * 4 + wl.B * 4
+               + 2 * wl.B * wl.Hq * wl.D * 2)
+
+
+def attn_cpu_baseline(wl, x, h, rot, budget_s=12.0):
+    """The float64 oracle, untuned, on the first sequences of the batch until
+    about `budget_s` seconds of work."""
+    from oracle import sawint4 as O
+    t0 = time.perf_counter()
+    n, toks = 0, 0
+    while n < wl.B and time.perf_counter() - t0 < budget_s:
+        O.paged_decode_attention(x["q"][n:n + 1], x["k_codes"], x["k_scales"], x["v_codes"],
+                                 x["v_scales"], x["block_tables"][n:n + 1],
+                                 x["context_lens"][n:n + 1], h=h, rot_mode=rot)
+        toks += int(x["context_lens"][n])
+        n += 1
+    dt = time.perf_counter() - t0
+    gbps = toks * wl.bytes_per_token() / dt / 1e9
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "decode_tokens_per_s": round(n / dt, 2), "seconds": round(dt, 2),
+            "sample": f"first {n} of {wl.B} sequences ({toks} context tokens) of the attn "
+                      f"batch, numpy float64 oracle, single thread"}
+
+
+def bench_attention(args):
+    import torch
+    from int4_kv_cache_amd import sawkv as S
+
+    wl = W.ATTN_WORKLOADS["attn"]
+    h = args.h or wl.h
+    rot = {"none": 0, "k": 1, "kv": 2}[args.rot] if args.rot else wl.rot_mode
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating attn inputs", file=sys.stderr, flush=True)
+    x = W.attn_inputs(wl)
+    d = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in x.items()}
+    pools = (d["k_codes"], d["v_codes"], d["k_scales"], d["v_scales"])
+    L = x["context_lens"]
+    maxc = int(L.max())
+    stream = torch.cuda.current_stream()
+    call = S.AttentionCall(d["q"], pools, d["block_tables"], d["context_lens"], maxc, h=h,
+                           rot=ROT_NAME[rot])
+    naive = S.AttentionCall(d["q"], pools, d["block_tables"], d["context_lens"], maxc, h=h,
+                            rot="none", workspace=call.workspace)
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    event_ms = e0.elapsed_time(e1) / args.steps
+    nbytes = attn_bytes(wl, x)
+    gbps = nbytes / (wall_ms * 1e-3) / 1e9
+    achieved = nbytes / (event_ms * 1e-3) / 1e9
+
+    rounds, n_ab = 7, max(20, args.steps // 4)
+    rot_ms, naive_ms = [], []
+    for _ in range(rounds):
+        naive_ms.append(timed(naive, n_ab))
+        rot_ms.append(timed(call, n_ab))
+    ratio = float(np.median(rot_ms) / np.median(naive_ms))
+
+    traffic = measured_traffic("attn", ATTN_SRC)
+    out = {
+        "metric": ATTN_METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": (f"attn: {wl.B} sequences x 1 query token, contexts uniform "
+                                f"in [{wl.ctx[1]}, {wl.ctx[2]}] ({int(L.sum())} tokens, max "
+                                f"{maxc}), {wl.Hq} query / {wl.H} KV heads x {wl.D}, page "
+                                f"{wl.P}, INT4 pool rotation {ROT_NAME[rot]} h={h}"),
+                   "sequences": wl.B, "context_tokens": int(L.sum()), "max_context": maxc,
+                   "query_heads": wl.Hq, "kv_heads": wl.H, "head_dim": wl.D,
+                   "page_size": wl.P, "rotation": ROT_NAME[rot], "block_size_h": h,
+                   "parallelism": "single GPU"},
+        "step": "sawkv_decode_attention: query prep + chunk kernel + combine (3 launches)",
+        "decode_tokens_per_s": round(wl.B / (wall_ms * 1e-3), 1),
+        "context_tokens_per_s": round(int(L.sum()) / (wall_ms * 1e-3), 1),
+        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,
+                     "kernel": "one sawkv_decode_attention call (attn_prep_kernel + "
+                               "attn_chunk_kernel + attn_combine_kernel)"},
+        "vs_naive": {"rot_ms_median": round(float(np.median(rot_ms)), 5),
+                     "naive_ms_median": round(float(np.median(naive_ms)), 5),
+                     "rot_over_naive": round(ratio, 4), "rounds": rounds,
+                     "steps_per_round": n_ab},
+        "workspace_bytes": int(call.workspace.numel()),
+        "kernel_source_hash": kernel_source_hash(ATTN_SRC),
+    }
+    if not args.no_cpu:
+        print("[bench] cpu baseline: oracle attention on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = attn_cpu_baseline(wl, x, h, rot)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="prefill", choices=["prefill", "decode", "sweep", "long"])
+    ap.add_argument("--workload", default="prefill",
+                    choices=["prefill", "decode", "sweep", "long", "attn"])
     ap.add_argument("--h", type=int, default=None)
     ap.add_argument("--rot", default=None, choices=["none", "k", "kv"])
     ap.add_argument("--cpu-sample", type=int, default=131072)
@@ -161,6 +302,10 @@ def main():
               "step, so a multi-GPU figure is not produced (run with --gpus 1).",
               file=sys.stderr, flush=True)
         sys.exit(2)
+
+    if args.workload == "attn":
+        bench_attention(args)
+        return
 
     import torch
     from int4_kv_cache_amd import sawkv as S

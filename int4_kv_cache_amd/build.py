@@ -6,7 +6,7 @@ Compiles int4_kv_cache_amd/csrc/sawkv.hip (write path and read-back) and
 sawkv_attn.hip (decode attention) into int4_kv_cache_amd/libsawkv.so.
 Flags: -ffp-contract=off (every float32 operation rounds on its own, as the
 bit-exact definition needs), no fast-math, denormals kept (the HIP default),
-and packed-fp32 instructions disabled.
+packed-fp32 instructions disabled, MFMA accumulators in VGPRs.
 """
 import os
 import shutil
@@ -32,6 +32,9 @@ def flags():
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-ffp-contract=off",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # keep matrix-core accumulators in VGPRs (the attention loop rescales
+        # them with VALU ops; AGPR accumulators would be copied every step)
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I", os.path.join(ROOT, "include"),
         "-I", os.path.join(PKG, "csrc"),
     ]

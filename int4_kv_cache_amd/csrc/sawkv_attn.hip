@@ -262,9 +262,198 @@ struct ChunkParams {
   uint32_t n_groups;       // B * NC
 };
 
+// Registers of one 32-token step as loaded from memory (tiles T = 0, 1 of 16
+// tokens; lane (g, n) = (lane / 16, lane % 16)).
+struct StepRegs {
+  u4_t kq[2];          // K codes of token n of tile T, bytes 16g..16g+15
+  uint32_t vd[2][4];   // V code dword n of token 4g + j of tile T
+  uint32_t sc;         // one scale: K (lanes 0-31) or V (lanes 32-63) of token
+                       // lane % 16 of tile (lane / 16) % 2
+  bool ok[2];          // tile starts before the end and has a valid page
+};
+
+// Per-lane constants of the chunk loop.
+struct Lanes {
+  uint32_t k_off;      // byte offset of the lane's K code bytes in a tile
+  uint32_t v_off[4];   // byte offsets of the lane's V code dwords
+  const uint16_t* s_ptr;  // the lane's scale pool (K for lanes 0-31, else V),
+                          // advanced to token lane % 16 of a tile
+  bool s_tile1;        // the lane stages a scale of tile 1 (else tile 0)
+};
+
+// Buffer resource over [base, base + bytes): raw (untyped) loads with the
+// hardware range check, which returns 0 past the end.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Issues the loads of the step at t0 into r. `pages` holds the page id of
+// block (blk0 + lane) of the sequence in lane `lane`.
+__device__ __forceinline__ void load_step(const ChunkParams& p, StepRegs& r, int t0, int t_end,
+                                          int blk0, int pages, int h, const Lanes& ln) {
+  const uint32_t row_bytes = (uint32_t)p.H * (kD / 2);
+  const uint32_t tile_bytes = 15u * row_bytes + kD / 2;      // reach of a lane's offsets
+  int64_t row[2];                                 // first row of each tile (0 if invalid)
+#pragma unroll
+  for (int T = 0; T < 2; ++T) {
+    const int st = t0 + 16 * T;
+    int page = -1;
+    if (st < t_end) page = __builtin_amdgcn_readlane(pages, st / p.P - blk0);
+    r.ok[T] = page >= 0 && page < p.N_pg;
+    row[T] = 0;
+    if (r.ok[T]) {
+      const int64_t row0 = ((int64_t)page * p.P + st % p.P) * p.H + h;
+      row[T] = row0;
+      const __amdgpu_buffer_rsrc_t rk = rsrc(p.k_codes + row0 * (kD / 2), tile_bytes);
+      const __amdgpu_buffer_rsrc_t rv = rsrc(p.v_codes + row0 * (kD / 2), tile_bytes);
+      r.kq[T] = __builtin_amdgcn_raw_buffer_load_b128(rk, ln.k_off, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        r.vd[T][j] = __builtin_amdgcn_raw_buffer_load_b32(rv, ln.v_off[j], 0, 0);
+    } else {
+      r.kq[T] = u4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r.vd[T][j] = 0u;
+    }
+  }
+  // one scale per lane; an invalid tile reads its lane's slot of row 0
+  // (in bounds, ignored)
+  r.sc = ln.s_ptr[ln.s_tile1 ? row[1] : row[0]];
+}
+
+template <int G>
+struct Acc {
+  float m, mref, l, W;
+  f4_t o[8];
+};
+
+__device__ __forceinline__ _Float16 half_lo(uint32_t x) {
+  return __builtin_bit_cast(_Float16, (uint16_t)(x & 0xFFFFu));
+}
+__device__ __forceinline__ _Float16 half_hi(uint32_t x) {
+  return __builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
+}
+
+// One 32-token step. ks[T] / vs[T]: the K / V scales of tokens 4g..4g+3 of
+// tile T as two dwords of fp16 pairs. mask: some tokens may be invalid.
+template <int G>
+__device__ __forceinline__ void compute_step(const StepRegs& r, const uint32_t (&ks)[2][2],
+                                             const uint32_t (&vs)[2][2], const u4_t (&bq)[4],
+                                             float cinit, float F, float F4, Acc<G>& a, int g,
+                                             int n, int t0, int t_end, bool mask) {
+  float lam[2][4], mu[2][4];
+#pragma unroll
+  for (int T = 0; T < 2; ++T) {
+    f4_t acc = f4_t{cinit, cinit, cinit, cinit};
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const uint32_t w = r.kq[T][cc] ^ 0x88888888u;
+      const uint32_t w8 = w >> 8;
+      const u4_t av = u4_t{w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu,
+                           w8 & 0x00F000F0u};
+      acc = mfma(av, bq[cc], acc);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float s = acc[j] + row_shl<G>(acc[j]);
+      const uint32_t kw = ks[T][j >> 1], vw = vs[T][j >> 1];
+      lam[T][j] = fmaf((float)((j & 1) ? half_hi(kw) : half_lo(kw)), s, 0.0f);
+      const float ub = (float)((j & 1) ? (vw >> 24) : ((vw >> 8) & 0xFFu));
+      mu[T][j] = fmaf(F4, lam[T][j], ub);
+    }
+  }
+  if (mask) {
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (!(r.ok[T] && t0 + 16 * T + 4 * g + j < t_end)) mu[T][j] = -INFINITY;
+  }
+
+  float mx = fmaxf(fmaxf(fmaxf(mu[0][0], mu[0][1]), fmaxf(mu[0][2], mu[0][3])),
+                   fmaxf(fmaxf(mu[1][0], mu[1][1]), fmaxf(mu[1][2], mu[1][3])));
+  mx = rows_max(mx);
+  const bool need = n < G && mx > a.m + 32.0f;
+  if (__any(need)) {
+    const float mn = need ? mx : a.m;
+    const float alpha = need ? __builtin_amdgcn_exp2f((a.m - mn) * 0.25f) : 1.0f;
+    a.l *= alpha;
+    a.W *= alpha;
+    float al[G];
+#pragma unroll
+    for (int qc = 0; qc < G; ++qc)
+      al[qc] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                             __builtin_bit_cast(int, alpha), qc));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float f;
+      if constexpr (G == 8) f = (g & 1) ? al[4 + j] : al[j];
+      else f = al[j % G];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) a.o[k][j] *= f;
+    }
+    a.m = mn;
+    a.mref = mn * 0.25f - 20.0f;
+  }
+
+  // weights p * s_v, split into fp16 hi + lo for the A operand
+  float pr[2][4], w[2][4];
+#pragma unroll
+  for (int T = 0; T < 2; ++T)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pr[T][j] = __builtin_amdgcn_exp2f(fmaf(F, lam[T][j], -a.mref));
+      const uint32_t vw = vs[T][j >> 1];
+      w[T][j] = fmaf((float)((j & 1) ? half_hi(vw) : half_lo(vw)), pr[T][j], 0.0f);
+    }
+  if (mask) {
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (!(r.ok[T] && t0 + 16 * T + 4 * g + j < t_end)) pr[T][j] = w[T][j] = 0.0f;
+  }
+#pragma unroll
+  for (int T = 0; T < 2; ++T)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a.l += pr[T][j];
+      a.W += w[T][j];
+    }
+  u4_t A;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int T = e >> 1, j0 = 2 * (e & 1);
+    const h2_t hi = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(w[T][j0], w[T][j0 + 1]));
+    const float r0 = fmaf((float)hi[0], -1.0f, w[T][j0]);
+    const float r1 = fmaf((float)hi[1], -1.0f, w[T][j0 + 1]);
+    const h2_t lo = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+    A[e] = lo_rows<G>(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo));
+  }
+
+  // values: lane n holds code dword n of tokens (T, j); MFMA 2*beta (+1) uses
+  // the low (high) nibble of byte beta
+#pragma unroll
+  for (int beta = 0; beta < 4; ++beta) {
+    const uint32_t sel = (uint32_t)beta | (0x0Cu << 8) | ((4u + beta) << 16) | (0x0Cu << 24);
+    u4_t blo, bhi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int T = e >> 1, j0 = 2 * (e & 1);
+      const uint32_t x = __builtin_amdgcn_perm(r.vd[T][j0 + 1], r.vd[T][j0], sel) ^ 0x00880088u;
+      blo[e] = x & 0x000F000Fu;
+      bhi[e] = x & 0x00F000F0u;
+    }
+    a.o[2 * beta] = mfma(A, blo, a.o[2 * beta]);
+    a.o[2 * beta + 1] = mfma(A, bhi, a.o[2 * beta + 1]);
+  }
+}
+
 template <int G>
 __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
+  __shared__ uint16_t sstage[64];
   const int lane = threadIdx.x;
   const int g = lane >> 4, n = lane & 15;
 
@@ -273,9 +462,9 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
   // consecutive blocks of one XCD, so the 64-byte rows of neighbouring heads,
   // which share cache lines, meet in one L2.
   const uint32_t bx = blockIdx.x;
-  const uint32_t r = bx >> 3;
-  const int h = (int)(r % (uint32_t)p.H);
-  const uint32_t grp = (r / (uint32_t)p.H) * 8u + (bx & 7u);
+  const uint32_t r8 = bx >> 3;
+  const int h = (int)(r8 % (uint32_t)p.H);
+  const uint32_t grp = (r8 / (uint32_t)p.H) * 8u + (bx & 7u);
   if (grp >= p.n_groups) return;
   const int b = (int)(grp / (uint32_t)p.NC), c = (int)(grp % (uint32_t)p.NC);
   int L = p.context_lens[b];
@@ -283,6 +472,11 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
   const int t_begin = c * p.C;
   if (t_begin >= L) return;
   const int t_end = min(t_begin + p.C, L);
+
+  // page ids of the chunk's blocks, one per lane (at most C / 16 + 1 <= 33)
+  const int blk0 = t_begin / p.P;
+  const int n_blk = (t_end - 1) / p.P - blk0 + 1;
+  const int pages = lane < n_blk ? p.block_tables[(int64_t)b * p.bt_stride + blk0 + lane] : -1;
 
   const int64_t bh = (int64_t)b * p.H + h;
   u4_t bq[4];
@@ -295,170 +489,66 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
   const float F = p.qconst[bh * 32 + 16 + n];
   const float F4 = 4.0f * F;
 
-  // lane offsets inside a 16-token tile (bytes for codes, elements for scales)
-  const int row_bytes = p.H * (kD / 2);
-  const int k_lane = n * row_bytes + 16 * g;
-  int v_lane[4], s_lane[4];
+  Lanes ln;
+  const uint32_t row_bytes = (uint32_t)p.H * (kD / 2);
+  ln.k_off = (uint32_t)n * row_bytes + 16u * (uint32_t)g;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    v_lane[j] = (4 * g + j) * row_bytes + 4 * n;
-    s_lane[j] = (4 * g + j) * p.H;
-  }
+  for (int j = 0; j < 4; ++j) ln.v_off[j] = (uint32_t)(4 * g + j) * row_bytes + 4u * (uint32_t)n;
+  ln.s_ptr = (lane < 32 ? p.k_scales : p.v_scales) + (int64_t)n * p.H;
+  ln.s_tile1 = (lane >> 4) & 1;
 
-  float m = -INFINITY, mref = 0.0f, l = 0.0f, W = 0.0f;
-  f4_t o[8];
+  Acc<G> a;
+  a.m = -INFINITY;
+  a.mref = 0.0f;
+  a.l = 0.0f;
+  a.W = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) o[k] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k = 0; k < 8; ++k) a.o[k] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int32_t* bt = p.block_tables + (int64_t)b * p.bt_stride;
-
+  // one step of look-ahead: the loads of step t0 + 32 are in flight while
+  // step t0 is computed
+  StepRegs cur, nxt;
+  load_step(p, cur, t_begin, t_end, blk0, pages, h, ln);
   for (int t0 = t_begin; t0 < t_end; t0 += kStep) {
-    bool ok[2];
-    u4_t kq[2];
-    uint32_t vd[2][4], sk[2][4], sv[2][4];
+    const int t1 = t0 + kStep;
+    if (t1 < t_end) load_step(p, nxt, t1, t_end, blk0, pages, h, ln);
+    sstage[lane] = (uint16_t)cur.sc;
+    __builtin_amdgcn_wave_barrier();
+    uint32_t ks[2][2], vs[2][2];
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
-      const int st = t0 + 16 * T;
-      const int page = st < t_end ? bt[st / p.P] : -1;
-      ok[T] = page >= 0 && page < p.N_pg;
-      if (ok[T]) {
-        const int64_t slot0 = (int64_t)page * p.P + st % p.P;
-        const int64_t row0 = slot0 * p.H + h;
-        const uint8_t* kb = p.k_codes + row0 * (kD / 2);
-        const uint8_t* vb = p.v_codes + row0 * (kD / 2);
-        kq[T] = *reinterpret_cast<const u4_t*>(kb + k_lane);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          vd[T][j] = *reinterpret_cast<const uint32_t*>(vb + v_lane[j]);
-          sk[T][j] = p.k_scales[row0 + s_lane[j]];
-          sv[T][j] = p.v_scales[row0 + s_lane[j]];
-        }
-      } else {
-        kq[T] = u4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) vd[T][j] = sk[T][j] = sv[T][j] = 0u;
-      }
+      const uint2 kk = *reinterpret_cast<const uint2*>(&sstage[16 * T + 4 * g]);
+      const uint2 vv = *reinterpret_cast<const uint2*>(&sstage[32 + 16 * T + 4 * g]);
+      ks[T][0] = kk.x;
+      ks[T][1] = kk.y;
+      vs[T][0] = vv.x;
+      vs[T][1] = vv.y;
     }
-    const bool full = ok[0] && ok[1] && t0 + kStep <= t_end;
-
-    // scores: columns n < G hold hi, G <= n < 2G lo; add them with a row shift
-    float lam[2][4], mu[2][4];
-#pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      f4_t acc = f4_t{cinit, cinit, cinit, cinit};
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const uint32_t w = kq[T][cc] ^ 0x88888888u;
-        const uint32_t w8 = w >> 8;
-        const u4_t a = u4_t{w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu,
-                            w8 & 0x00F000F0u};
-        acc = mfma(a, bq[cc], acc);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float s = acc[j] + row_shl<G>(acc[j]);
-        lam[T][j] = s * half_bits_to_float(sk[T][j]);
-        mu[T][j] = fmaf(F4, lam[T][j], (float)((sv[T][j] >> 8) & 0xFFu));
-      }
-    }
-    bool valid[2][4];
-#pragma unroll
-    for (int T = 0; T < 2; ++T)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        valid[T][j] = full || (ok[T] && t0 + 16 * T + 4 * g + j < t_end);
-        if (!valid[T][j]) mu[T][j] = -INFINITY;
-      }
-
-    float mx = fmaxf(fmaxf(fmaxf(mu[0][0], mu[0][1]), fmaxf(mu[0][2], mu[0][3])),
-                     fmaxf(fmaxf(mu[1][0], mu[1][1]), fmaxf(mu[1][2], mu[1][3])));
-    mx = rows_max(mx);
-    const bool need = n < G && mx > m + 32.0f;
-    if (__any(need)) {
-      const float mn = need ? mx : m;
-      const float alpha = need ? __builtin_amdgcn_exp2f((m - mn) * 0.25f) : 1.0f;
-      l *= alpha;
-      W *= alpha;
-      float al[G];
-#pragma unroll
-      for (int qc = 0; qc < G; ++qc)
-        al[qc] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                               __builtin_bit_cast(int, alpha), qc));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float a;
-        if constexpr (G == 8) a = (g & 1) ? al[4 + j] : al[j];
-        else a = al[j % G];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) o[k][j] *= a;
-      }
-      m = mn;
-      mref = m * 0.25f - 20.0f;
-    }
-
-    // weights p * s_v, split into fp16 hi + lo for the A operand
-    float w[2][4];
-#pragma unroll
-    for (int T = 0; T < 2; ++T)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float pr = __builtin_amdgcn_exp2f(fmaf(F, lam[T][j], -mref));
-        float ww = pr * half_bits_to_float(sv[T][j]);
-        if (!valid[T][j]) pr = ww = 0.0f;
-        l += pr;
-        W += ww;
-        w[T][j] = ww;
-      }
-    u4_t A;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int T = e >> 1, j0 = 2 * (e & 1);
-      const h2_t hi = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(w[T][j0], w[T][j0 + 1]));
-      const h2_t lo = __builtin_bit_cast(
-          h2_t, __builtin_amdgcn_cvt_pkrtz(w[T][j0] - (float)hi[0], w[T][j0 + 1] - (float)hi[1]));
-      A[e] = lo_rows<G>(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo));
-    }
-
-    // values: lane n holds code dword n of tokens (T, j); MFMA j' uses nibble j'
-#pragma unroll
-    for (int T = 0; T < 2; ++T)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vd[T][j] ^= 0x88888888u;
-#pragma unroll
-    for (int beta = 0; beta < 4; ++beta) {
-      const uint32_t sel = (uint32_t)beta | (0x0Cu << 8) | ((4u + beta) << 16) | (0x0Cu << 24);
-      u4_t blo, bhi;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int T = e >> 1, j0 = 2 * (e & 1);
-        const uint32_t x = __builtin_amdgcn_perm(vd[T][j0 + 1], vd[T][j0], sel);
-        blo[e] = x & 0x000F000Fu;
-        bhi[e] = x & 0x00F000F0u;
-      }
-      o[2 * beta] = mfma(A, blo, o[2 * beta]);
-      o[2 * beta + 1] = mfma(A, bhi, o[2 * beta + 1]);
-    }
+    __builtin_amdgcn_wave_barrier();
+    const bool mask = !(cur.ok[0] && cur.ok[1] && t1 <= t_end);
+    compute_step<G>(cur, ks, vs, bq, cinit, F, F4, a, g, n, t0, t_end, mask);
+    cur = nxt;
   }
 
   // ---- chunk partial ----
-  l = rows_sum(l);
-  W = rows_sum(W);
+  float l = rows_sum(a.l);
+  float W = rows_sum(a.W);
   f4_t os[8];
   if constexpr (G == 4 || G == 8) {
 #pragma unroll
     for (int k = 0; k < 8; ++k)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float a = o[k][j], b = o[k][j];
-        if constexpr (G == 4) swap16(a, b);
-        else swap32(a, b);
-        os[k][j] = a + b;
+        float x = a.o[k][j], y = a.o[k][j];
+        if constexpr (G == 4) swap16(x, y);
+        else swap32(x, y);
+        os[k][j] = x + y;
       }
   } else {
 #pragma unroll
     for (int k = 0; k < 8; ++k)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) os[k][j] = j < G ? o[k][j] + o[k][j + G] : 0.0f;
+      for (int j = 0; j < 4; ++j) os[k][j] = j < G ? a.o[k][j] + a.o[k][j + G] : 0.0f;
   }
   float Wq[G];
 #pragma unroll
@@ -484,7 +574,7 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
     }
   }
   if (g == 0 && n < G) {
-    p.part_ml[(head0 + n) * 2] = m == -INFINITY ? -INFINITY : mref;
+    p.part_ml[(head0 + n) * 2] = a.m == -INFINITY ? -INFINITY : a.mref;
     p.part_ml[(head0 + n) * 2 + 1] = l;
   }
 }
