@@ -20,8 +20,9 @@
 //           the matrix cores straight from the packed nibbles, an online
 //           softmax, and P.V on the matrix cores; writes the chunk's partial
 //           (reference exponent, denominator, unnormalised output).
-//  combine  one quad per (sequence, query head): merges the chunks, divides,
-//           un-rotates V (if rotated), rounds to fp16.
+//  combine  16 lanes per (sequence, query head): merge the chunks (four
+//           quads, each over every fourth chunk), divide, un-rotate V (if
+//           rotated), round to fp16.
 //
 // Nibbles on the matrix cores. A code byte holds two two's-complement
 // nibbles; xor 0x88 turns them into u = code + 8 in [0, 15]. Masking one
@@ -132,29 +133,46 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
 // prep: q -> B operand of the score MFMAs
 // ---------------------------------------------------------------------------
 
-struct PrepParams {
+struct QueryParams {
   const __half* q;
   int64_t q_stride;        // elements between the rows of two sequences
-  uint32_t* qprep;         // [B][H][64][16]
-  float* qconst;           // [B][H][2][16]: C-init column values, log2 scale F
-  int32_t H;
   int32_t h;
   int32_t rot_k;
   float c_h;               // f32(1/sqrt(h))
   float c_sm;              // sm_scale * log2(e)
 };
 
-template <int G>
-__global__ __launch_bounds__(64) void attn_prep_kernel(PrepParams p) {
-  __shared__ float xs[G][kD];
-  const int lane = threadIdx.x;
-  const int64_t bh = blockIdx.x;
-  const int64_t b = bh / p.H;
-  const int h = (int)(bh % p.H);
+// Column n of the score MFMAs' B operand holds (query of the block, part):
+//   single head (PAIR false): n < G hi of query n, G <= n < 2G lo of query n - G
+//   head pair (PAIR true, G = 4): query 4 (n / 8) + n % 4, lo when n & 4
+// where the block's queries are those of its heads in order.
+template <int G, bool PAIR>
+__device__ __forceinline__ int column_query(int n) {
+  if constexpr (PAIR) return 4 * (n >> 3) + (n & 3);
+  else return n < G ? n : (n < 2 * G ? n - G : -1);
+}
+template <int G, bool PAIR>
+__device__ __forceinline__ bool column_hi(int n) {
+  if constexpr (PAIR) return (n & 4) == 0;
+  else return n < G;
+}
+
+// The B operand of the score MFMAs for the calling lane (bq), and for the
+// lane's column n = lane % 16 the accumulator start value (minus 8 times the
+// sum of the query's effective multipliers, cinit) and the log2-unit scale F.
+// The wave's queries are those of head group `hg` of sequence b: one KV head,
+// or a pair of KV heads (PAIR). xs: NQ x 128 floats of LDS. One wave.
+template <int G, bool PAIR>
+__device__ __forceinline__ void prepare_query(const QueryParams& p, int64_t b, int hg, int lane,
+                                              float (*xs)[kD], u4_t (&bq)[4], float& cinit_n,
+                                              float& F_n) {
+  constexpr int NQ = PAIR ? 2 * G : G;          // queries of the wave
+  static_assert(!PAIR || G == 4, "head pairs are laid out for 4 queries per head");
+  const int h = hg;
 
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const __half* row = p.q + b * p.q_stride + (int64_t)(h * G + g) * kD;
+  for (int g = 0; g < NQ; ++g) {
+    const __half* row = p.q + b * p.q_stride + (int64_t)(h * NQ + g) * kD;
     xs[g][2 * lane] = __half2float(row[2 * lane]);
     xs[g][2 * lane + 1] = __half2float(row[2 * lane + 1]);
   }
@@ -165,7 +183,7 @@ __global__ __launch_bounds__(64) void attn_prep_kernel(PrepParams p) {
     for (int s = 1; s < p.h; s <<= 1) {
       const int i = (lane / s) * 2 * s + (lane % s);
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
+      for (int g = 0; g < NQ; ++g) {
         const float a = xs[g][i], c = xs[g][i + s];
         xs[g][i] = a + c;
         xs[g][i + s] = a - c;
@@ -175,18 +193,25 @@ __global__ __launch_bounds__(64) void attn_prep_kernel(PrepParams p) {
   }
   const float mul = p.rot_k ? p.c_h : 1.0f;
 
-  float sig_scale[G], cinit[G];
+  // all queries' reductions side by side (independent shuffle chains)
+  float v0[NQ], v1[NQ], amax[NQ];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float v0 = xs[g][2 * lane] * mul * p.c_sm;
-    const float v1 = xs[g][2 * lane + 1] * mul * p.c_sm;
-    float amax = fmaxf(fabsf(v0), fabsf(v1));
+  for (int g = 0; g < NQ; ++g) {
+    v0[g] = xs[g][2 * lane] * mul * p.c_sm;
+    v1[g] = xs[g][2 * lane + 1] * mul * p.c_sm;
+    amax[g] = fmaxf(fabsf(v0[g]), fabsf(v1[g]));
+  }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+    for (int g = 0; g < NQ; ++g) amax[g] = fmaxf(amax[g], __shfl_xor(amax[g], o));
+  float sig_scale[NQ], cinit[NQ], msum[NQ];
+#pragma unroll
+  for (int g = 0; g < NQ; ++g) {
     int e = 0;
-    if (amax > 0.0f) frexpf(amax, &e);            // amax in [2^(e-1), 2^e)
-    const int sigma = amax > 0.0f ? 14 - e : 0;   // max |Q| in [2^13, 2^14)
-    const float Q0 = ldexpf(v0, sigma), Q1 = ldexpf(v1, sigma);
+    if (amax[g] > 0.0f) frexpf(amax[g], &e);         // amax in [2^(e-1), 2^e)
+    const int sigma = amax[g] > 0.0f ? 14 - e : 0;   // max |Q| in [2^13, 2^14)
+    const float Q0 = ldexpf(v0[g], sigma), Q1 = ldexpf(v1[g], sigma);
     // effective multiplier of u: (hi + lo) of Q (even channel) and of Q / 16
     // times 16 (odd channel)
     const _Float16 h0 = (_Float16)Q0;
@@ -194,14 +219,17 @@ __global__ __launch_bounds__(64) void attn_prep_kernel(PrepParams p) {
     const float q16 = Q1 * 0.0625f;
     const _Float16 h1 = (_Float16)q16;
     const _Float16 l1 = (_Float16)(q16 - (float)h1);
-    float msum = ((float)h0 + (float)l0) + 16.0f * ((float)h1 + (float)l1);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) msum += __shfl_xor(msum, o);
-    cinit[g] = -8.0f * ldexpf(msum, -24);
+    msum[g] = ((float)h0 + (float)l0) + 16.0f * ((float)h1 + (float)l1);
     sig_scale[g] = ldexpf(1.0f, 24 - sigma);
     xs[g][2 * lane] = Q0;                      // each lane rewrites its own two channels
     xs[g][2 * lane + 1] = q16;
   }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+    for (int g = 0; g < NQ; ++g) msum[g] += __shfl_xor(msum[g], o);
+#pragma unroll
+  for (int g = 0; g < NQ; ++g) cinit[g] = -8.0f * ldexpf(msum[g], -24);
   __syncthreads();
 
   const int gl = lane >> 4, n = lane & 15;
@@ -212,33 +240,34 @@ __global__ __launch_bounds__(64) void attn_prep_kernel(PrepParams p) {
     for (int e = 0; e < 4; ++e) {
       const int ch0 = 8 * (4 * gl + c) + e, ch1 = ch0 + 4;
       uint32_t w = 0;
-      if (n < 2 * G) {
-        const int qi = n < G ? n : n - G;
+      const int qi = column_query<G, PAIR>(n);
+      if (qi >= 0) {
         float v[2] = {xs[qi][ch0], xs[qi][ch1]};
         uint16_t bits[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const _Float16 hi = (_Float16)v[k];
           const _Float16 lo = (_Float16)(v[k] - (float)hi);
-          bits[k] = __builtin_bit_cast(uint16_t, n < G ? hi : lo);
+          bits[k] = __builtin_bit_cast(uint16_t, column_hi<G, PAIR>(n) ? hi : lo);
         }
         w = (uint32_t)bits[0] | ((uint32_t)bits[1] << 16);
       }
       words[4 * c + e] = w;
     }
   }
-  u4_t* dst = reinterpret_cast<u4_t*>(p.qprep + (bh * 64 + lane) * kQWords);
 #pragma unroll
   for (int k = 0; k < 4; ++k)
-    dst[k] = u4_t{words[4 * k], words[4 * k + 1], words[4 * k + 2], words[4 * k + 3]};
-  if (lane < 16) {
-    float ci = 0.0f, f = 0.0f;
+    bq[k] = u4_t{words[4 * k], words[4 * k + 1], words[4 * k + 2], words[4 * k + 3]};
+  float ci = 0.0f, f = 0.0f;
+  {
+    const int qi = column_query<G, PAIR>(n);
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-      if (lane == g) { ci = cinit[g]; f = sig_scale[g]; }
-    p.qconst[bh * 32 + lane] = ci;
-    p.qconst[bh * 32 + 16 + lane] = f;
+    for (int g = 0; g < NQ; ++g)
+      if (qi == g && column_hi<G, PAIR>(n)) { ci = cinit[g]; f = sig_scale[g]; }
   }
+  cinit_n = ci;
+  F_n = f;
+  __syncthreads();                 // xs is reused by the caller's next query group
 }
 
 // ---------------------------------------------------------------------------
@@ -253,8 +282,7 @@ struct ChunkParams {
   const int32_t* block_tables;
   int64_t bt_stride;
   const int32_t* context_lens;
-  const uint32_t* qprep;
-  const float* qconst;
+  QueryParams qp;
   float* part_o;           // [B][NC][Hq][128]
   float* part_ml;          // [B][NC][Hq][2]: reference exponent, denominator
   int64_t N_pg;
@@ -454,10 +482,11 @@ template <int G>
 __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
   __shared__ uint16_t sstage[64];
+  __shared__ float xs[G][kD];
   const int lane = threadIdx.x;
   const int g = lane >> 4, n = lane & 15;
 
-  // Block -> (sequence, chunk, head). Blocks are dealt to the 8 XCDs in turn
+  // Block -> (chunk, sequence, head). Blocks are dealt to the 8 XCDs in turn
   // (block i to XCD i % 8); the H heads of one (sequence, chunk) get
   // consecutive blocks of one XCD, so the 64-byte rows of neighbouring heads,
   // which share cache lines, meet in one L2.
@@ -466,7 +495,11 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
   const int h = (int)(r8 % (uint32_t)p.H);
   const uint32_t grp = (r8 / (uint32_t)p.H) * 8u + (bx & 7u);
   if (grp >= p.n_groups) return;
-  const int b = (int)(grp / (uint32_t)p.NC), c = (int)(grp % (uint32_t)p.NC);
+  // chunk-major: every sequence's first chunk, then every second chunk, ...,
+  // so the last blocks dispatched are the final chunks of the longest contexts
+  const uint32_t nb = p.n_groups / (uint32_t)p.NC;
+  const int c = (int)(grp / nb), b = (int)(grp % nb);
+  const uint32_t part = (uint32_t)b * p.NC + c;    // partial slot (b, c)
   int L = p.context_lens[b];
   L = L < 0 ? 0 : (L > p.max_context ? p.max_context : L);
   const int t_begin = c * p.C;
@@ -478,15 +511,9 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
   const int n_blk = (t_end - 1) / p.P - blk0 + 1;
   const int pages = lane < n_blk ? p.block_tables[(int64_t)b * p.bt_stride + blk0 + lane] : -1;
 
-  const int64_t bh = (int64_t)b * p.H + h;
   u4_t bq[4];
-  {
-    const u4_t* src = reinterpret_cast<const u4_t*>(p.qprep + (bh * 64 + lane) * kQWords);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) bq[k] = src[k];
-  }
-  const float cinit = p.qconst[bh * 32 + n];
-  const float F = p.qconst[bh * 32 + 16 + n];
+  float cinit, F;
+  prepare_query<G, false>(p.qp, b, h, lane, xs, bq, cinit, F);
   const float F4 = 4.0f * F;
 
   Lanes ln;
@@ -555,7 +582,7 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
   for (int qc = 0; qc < G; ++qc)
     Wq[qc] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, W), qc));
 
-  const int64_t head0 = (int64_t)grp * p.Hq + (int64_t)h * G;   // grp = b * NC + c
+  const int64_t head0 = (int64_t)part * p.Hq + (int64_t)h * G;
   const bool writer = G == 8 ? g < 2 : g == 0;
   if (writer) {
 #pragma unroll
@@ -580,6 +607,299 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// chunk, head pairs (G = 4): one wave per (sequence, chunk, pair of KV heads)
+// ---------------------------------------------------------------------------
+//
+// The two heads of a pair hold the two halves of one 128-byte cache line of
+// every token, so a wave that owns the pair reads whole lines. A step is 16
+// tokens (one page-aligned block) of both heads, as two tiles of 8 tokens.
+//
+// Scores: MFMA row m of tile tau is token 8 tau + 2 (m % 4) + m / 8 of head
+// (m / 4) % 2; columns 0-3 / 4-7 hold the hi / lo parts of head 0's four
+// queries, 8-11 / 12-15 those of head 1. Result lane (g, n) holds rows
+// 4g + j: tokens 8 tau + 2j + g / 2 of head g % 2, so its values are useful
+// when its column belongs to that head (n / 8 == g % 2, n % 8 < 4).
+// Values: k slot (g, i = 4 tau + j) is token 8 tau + 2j + g / 2 of head g % 2,
+// so the weights sit in the same lanes as their scores; rows 0-3 / 4-7 of the
+// A operand are head 0's hi / lo weights, rows 8-11 / 12-15 head 1's, and a
+// row is zero where the slot's head is not the row's head.
+
+struct PairLanes {
+  uint32_t k_off[2];   // byte offsets of the lane's K code bytes, tiles 0 and 1
+  uint32_t v_off[8];   // byte offsets of the lane's V code dwords, slots i
+  const uint16_t* s_ptr;  // the lane's scale (loader role), relative to the block
+};
+
+__device__ __forceinline__ void load_pair_step(const ChunkParams& p, StepRegs& r, int t0,
+                                               int t_end, int blk0, int pages, int h0,
+                                               const PairLanes& ln) {
+  const uint32_t row_bytes = (uint32_t)p.H * (kD / 2);
+  int page = -1;
+  if (t0 < t_end) page = __builtin_amdgcn_readlane(pages, t0 / p.P - blk0);
+  const bool ok = page >= 0 && page < p.N_pg;
+  r.ok[0] = r.ok[1] = ok;
+  int64_t row0 = 0;
+  if (ok) {
+    row0 = ((int64_t)page * p.P + t0 % p.P) * p.H + h0;
+    const uint32_t reach = 15u * row_bytes + 2u * (kD / 2);   // 16 tokens, two heads
+    const __amdgpu_buffer_rsrc_t rk = rsrc(p.k_codes + row0 * (kD / 2), reach);
+    const __amdgpu_buffer_rsrc_t rv = rsrc(p.v_codes + row0 * (kD / 2), reach);
+#pragma unroll
+    for (int T = 0; T < 2; ++T) r.kq[T] = __builtin_amdgcn_raw_buffer_load_b128(rk, ln.k_off[T], 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      r.vd[i >> 2][i & 3] = __builtin_amdgcn_raw_buffer_load_b32(rv, ln.v_off[i], 0, 0);
+  } else {
+#pragma unroll
+    for (int T = 0; T < 2; ++T) r.kq[T] = u4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.vd[i >> 2][i & 3] = 0u;
+  }
+  r.sc = ln.s_ptr[row0];       // an invalid block reads row 0 of the pool (ignored)
+}
+
+// One 16-token step of a head pair. ks[tau] / vs[tau]: the K / V scales of the
+// lane's rows (tokens 8 tau + 2j + g / 2, head g % 2, j = 0..3) as two dwords
+// of fp16 pairs. head_ok: the lane's column belongs to its rows' head.
+__device__ __forceinline__ void compute_pair_step(const StepRegs& r, const uint32_t (&ks)[2][2],
+                                                  const uint32_t (&vs)[2][2], const u4_t (&bq)[4],
+                                                  float cinit, float F, float F4, Acc<4>& a,
+                                                  int g, int n, bool head_ok, int t0, int t_end,
+                                                  bool mask) {
+  float lam[2][4], mu[2][4];
+#pragma unroll
+  for (int T = 0; T < 2; ++T) {
+    f4_t acc = f4_t{cinit, cinit, cinit, cinit};
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const uint32_t w = r.kq[T][cc] ^ 0x88888888u;
+      const uint32_t w8 = w >> 8;
+      const u4_t av = u4_t{w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu,
+                           w8 & 0x00F000F0u};
+      acc = mfma(av, bq[cc], acc);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float sc = acc[j] + row_shl<4>(acc[j]);
+      const uint32_t kw = ks[T][j >> 1], vw = vs[T][j >> 1];
+      lam[T][j] = fmaf((float)((j & 1) ? half_hi(kw) : half_lo(kw)), sc, 0.0f);
+      const float ub = (float)((j & 1) ? (vw >> 24) : ((vw >> 8) & 0xFFu));
+      mu[T][j] = fmaf(F4, lam[T][j], ub);
+    }
+  }
+  if (mask) {
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (!(r.ok[T] && t0 + 8 * T + 2 * j + (g >> 1) < t_end)) mu[T][j] = -INFINITY;
+  }
+
+  float mx = fmaxf(fmaxf(fmaxf(mu[0][0], mu[0][1]), fmaxf(mu[0][2], mu[0][3])),
+                   fmaxf(fmaxf(mu[1][0], mu[1][1]), fmaxf(mu[1][2], mu[1][3])));
+  mx = rows_max(head_ok ? mx : -INFINITY);
+  const bool need = (n & 4) == 0 && mx > a.m + 32.0f;
+  if (__any(need)) {
+    const float mn = need ? mx : a.m;
+    const float alpha = need ? __builtin_amdgcn_exp2f((a.m - mn) * 0.25f) : 1.0f;
+    a.l *= alpha;
+    a.W *= alpha;
+    float al[8];
+#pragma unroll
+    for (int qc = 0; qc < 8; ++qc)
+      al[qc] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                             __builtin_bit_cast(int, alpha), 8 * (qc >> 2) + (qc & 3)));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float f = (g >> 1) ? al[4 + j] : al[j];     // rows 4g + j: head g / 2, query j
+#pragma unroll
+      for (int k = 0; k < 8; ++k) a.o[k][j] *= f;
+    }
+    a.m = mn;
+    a.mref = mn * 0.25f - 20.0f;
+  }
+
+  float pr[2][4], w[2][4];
+#pragma unroll
+  for (int T = 0; T < 2; ++T)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pr[T][j] = __builtin_amdgcn_exp2f(fmaf(F, lam[T][j], -a.mref));
+      const uint32_t vw = vs[T][j >> 1];
+      w[T][j] = fmaf((float)((j & 1) ? half_hi(vw) : half_lo(vw)), pr[T][j], 0.0f);
+    }
+  if (mask) {
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (!(r.ok[T] && t0 + 8 * T + 2 * j + (g >> 1) < t_end)) pr[T][j] = w[T][j] = 0.0f;
+  }
+#pragma unroll
+  for (int T = 0; T < 2; ++T)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a.l += pr[T][j];
+      a.W += w[T][j];
+    }
+  u4_t A;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int T = e >> 1, j0 = 2 * (e & 1);
+    const h2_t hi = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(w[T][j0], w[T][j0 + 1]));
+    const float r0 = fmaf((float)hi[0], -1.0f, w[T][j0]);
+    const float r1 = fmaf((float)hi[1], -1.0f, w[T][j0 + 1]);
+    const h2_t lo = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+    // lanes 4-7 and 12-15 of each row take the lo part from lane - 4
+    const uint32_t v = (uint32_t)__builtin_amdgcn_update_dpp(
+        (int)__builtin_bit_cast(uint32_t, hi), (int)__builtin_bit_cast(uint32_t, lo), 0x114, 0xF,
+        0xA, false);
+    A[e] = head_ok ? v : 0u;
+  }
+
+#pragma unroll
+  for (int beta = 0; beta < 4; ++beta) {
+    const uint32_t sel = (uint32_t)beta | (0x0Cu << 8) | ((4u + beta) << 16) | (0x0Cu << 24);
+    u4_t blo, bhi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int T = e >> 1, j0 = 2 * (e & 1);
+      const uint32_t x = __builtin_amdgcn_perm(r.vd[T][j0 + 1], r.vd[T][j0], sel) ^ 0x00880088u;
+      blo[e] = x & 0x000F000Fu;
+      bhi[e] = x & 0x00F000F0u;
+    }
+    a.o[2 * beta] = mfma(A, blo, a.o[2 * beta]);
+    a.o[2 * beta + 1] = mfma(A, bhi, a.o[2 * beta + 1]);
+  }
+}
+
+__global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
+  constexpr int G = 4;
+  __shared__ uint16_t sstage[64];
+  __shared__ float xs[2 * G][kD];
+  const int lane = threadIdx.x;
+  const int g = lane >> 4, n = lane & 15;
+  const int HP = p.H / 2;
+
+  // Block -> (chunk, sequence, head pair), the pairs of one (sequence, chunk)
+  // on consecutive blocks of one XCD.
+  const uint32_t bx = blockIdx.x;
+  const uint32_t r8 = bx >> 3;
+  const int hp = (int)(r8 % (uint32_t)HP);
+  const uint32_t grp = (r8 / (uint32_t)HP) * 8u + (bx & 7u);
+  if (grp >= p.n_groups) return;
+  // chunk-major: every sequence's first chunk, then every second chunk, ...,
+  // so the last blocks dispatched are the final chunks of the longest contexts
+  const uint32_t nb = p.n_groups / (uint32_t)p.NC;
+  const int c = (int)(grp / nb), b = (int)(grp % nb);
+  const uint32_t part = (uint32_t)b * p.NC + c;    // partial slot (b, c)
+  int L = p.context_lens[b];
+  L = L < 0 ? 0 : (L > p.max_context ? p.max_context : L);
+  const int t_begin = c * p.C;
+  if (t_begin >= L) return;
+  const int t_end = min(t_begin + p.C, L);
+  const int h0 = 2 * hp;
+
+  const int blk0 = t_begin / p.P;
+  const int n_blk = (t_end - 1) / p.P - blk0 + 1;
+  const int pages = lane < n_blk ? p.block_tables[(int64_t)b * p.bt_stride + blk0 + lane] : -1;
+
+  u4_t bq[4];
+  float cinit, F;
+  prepare_query<G, true>(p.qp, b, hp, lane, xs, bq, cinit, F);
+  const float F4 = 4.0f * F;
+  const bool head_ok = (n >> 3) == (g & 1);
+
+  PairLanes ln;
+  const uint32_t row_bytes = (uint32_t)p.H * (kD / 2);
+#pragma unroll
+  for (int T = 0; T < 2; ++T)
+    ln.k_off[T] = (uint32_t)(8 * T + 2 * (n & 3) + (n >> 3)) * row_bytes +
+                  (uint32_t)((n >> 2) & 1) * (kD / 2) + 16u * (uint32_t)g;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    ln.v_off[i] = (uint32_t)(8 * (i >> 2) + 2 * (i & 3) + (g >> 1)) * row_bytes +
+                  (uint32_t)(g & 1) * (kD / 2) + 4u * (uint32_t)n;
+  {
+    // loader role: lane l stages tensor l / 32 (K, V), tile (l / 16) % 2, and
+    // the reader slot (g' = (l / 4) % 4, j = l % 4): token 8 tau + 2j + g' / 2
+    // of head g' % 2
+    const int tau = (lane >> 4) & 1, gs = (lane >> 2) & 3, js = lane & 3;
+    ln.s_ptr = (lane < 32 ? p.k_scales : p.v_scales) +
+               (int64_t)(8 * tau + 2 * js + (gs >> 1)) * p.H + (gs & 1);
+  }
+
+  Acc<G> a;
+  a.m = -INFINITY;
+  a.mref = 0.0f;
+  a.l = 0.0f;
+  a.W = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) a.o[k] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  StepRegs cur, nxt;
+  load_pair_step(p, cur, t_begin, t_end, blk0, pages, h0, ln);
+  for (int t0 = t_begin; t0 < t_end; t0 += 16) {
+    const int t1 = t0 + 16;
+    if (t1 < t_end) load_pair_step(p, nxt, t1, t_end, blk0, pages, h0, ln);
+    sstage[lane] = (uint16_t)cur.sc;
+    __builtin_amdgcn_wave_barrier();
+    uint32_t ks[2][2], vs[2][2];
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      const uint2 kk = *reinterpret_cast<const uint2*>(&sstage[16 * T + 4 * g]);
+      const uint2 vv = *reinterpret_cast<const uint2*>(&sstage[32 + 16 * T + 4 * g]);
+      ks[T][0] = kk.x;
+      ks[T][1] = kk.y;
+      vs[T][0] = vv.x;
+      vs[T][1] = vv.y;
+    }
+    __builtin_amdgcn_wave_barrier();
+    const bool mask = !(cur.ok[0] && t1 <= t_end);
+    compute_pair_step(cur, ks, vs, bq, cinit, F, F4, a, g, n, head_ok, t0, t_end, mask);
+    cur = nxt;
+  }
+
+  // ---- chunk partial ----
+  const float l = rows_sum(head_ok && (n & 4) == 0 ? a.l : 0.0f);
+  const float W = rows_sum(head_ok && (n & 4) == 0 ? a.W : 0.0f);
+  f4_t os[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float x = a.o[k][j], y = a.o[k][j];
+      swap16(x, y);                       // rows 4g + j: hi (g even) + lo (g odd)
+      os[k][j] = x + y;
+    }
+  float Wq[8];
+#pragma unroll
+  for (int qc = 0; qc < 8; ++qc)
+    Wq[qc] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, W),
+                                                                 8 * (qc >> 2) + (qc & 3)));
+  const int64_t head0 = (int64_t)part * p.Hq + (int64_t)h0 * G;
+  if ((g & 1) == 0) {                       // g = 0: head 0, g = 2: head 1
+    const int hh = g >> 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float Wv = hh ? Wq[4 + j] : Wq[j];
+      float vals[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        vals[k] = os[k][j] * ((k & 1) ? 1048576.0f : 16777216.0f) - 8.0f * Wv;
+      f4_t* dst = reinterpret_cast<f4_t*>(p.part_o + (head0 + 4 * hh + j) * kD + 8 * n);
+      dst[0] = f4_t{vals[0], vals[1], vals[2], vals[3]};
+      dst[1] = f4_t{vals[4], vals[5], vals[6], vals[7]};
+    }
+  }
+  if (g == 0 && (n & 4) == 0) {
+    const int64_t qrow = head0 + 4 * (n >> 3) + (n & 3);
+    p.part_ml[qrow * 2] = a.m == -INFINITY ? -INFINITY : a.mref;
+    p.part_ml[qrow * 2 + 1] = l;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // combine: merge chunks, normalise, un-rotate V, fp16
 // ---------------------------------------------------------------------------
 
@@ -592,10 +912,27 @@ struct CombineParams {
   int32_t Hq, NC, C, max_context;
 };
 
+// Sum of v over the four quads of a row of 16 lanes (DPP row rotations by 4,
+// 8 and 12); every lane of the row gets the total.
+__device__ __forceinline__ float quads_sum(float v) {
+  const int b = __builtin_bit_cast(int, v);
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0x124, 0xF, 0xF, false)) +
+         __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0x128, 0xF, 0xF, false)) +
+         __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0x12C, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quads_max(float v) {
+  const int b = __builtin_bit_cast(int, v);
+  return fmaxf(fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0x124, 0xF, 0xF, false))),
+               fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0x128, 0xF, 0xF, false)),
+                     __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0x12C, 0xF, 0xF, false))));
+}
+
+// One row of 16 lanes per output vector (4 vectors per wave): quad qd of the
+// row merges chunks qd, qd + 4, ...; the four quads are then merged.
 template <int HB>
 __global__ __launch_bounds__(64) void attn_combine_kernel(CombineParams p) {
-  const int lane = threadIdx.x, lam = lane & 3;
-  const int64_t v = (int64_t)blockIdx.x * 16 + (lane >> 2);
+  const int lane = threadIdx.x, lam = lane & 3, qd = (lane >> 2) & 3;
+  const int64_t v = (int64_t)blockIdx.x * 4 + (lane >> 4);
   const bool live = v < p.n_vec;
   const int64_t b = live ? v / p.Hq : 0;
   const int qh = live ? (int)(v % p.Hq) : 0;
@@ -604,32 +941,66 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(CombineParams p) {
   const int nck = (L + p.C - 1) / p.C;
   const int64_t base = b * p.NC * p.Hq + qh;      // chunk c adds c * Hq
 
+  // running reference M: a chunk with a larger one rescales what is summed
   float M = -INFINITY;
-  for (int c = 0; c < nck; ++c) M = fmaxf(M, p.part_ml[(base + (int64_t)c * p.Hq) * 2]);
-
   float x[kElems];
 #pragma unroll
   for (int k = 0; k < kElems; ++k) x[k] = 0.0f;
   float lsum = 0.0f;
-  if (M > -INFINITY) {
-    for (int c = 0; c < nck; ++c) {
-      const int64_t row = base + (int64_t)c * p.Hq;
-      const float ref = p.part_ml[row * 2];
-      if (ref == -INFINITY) continue;
-      const float sc = __builtin_amdgcn_exp2f(ref - M);
-      lsum += sc * p.part_ml[row * 2 + 1];
+  const int mine = nck > qd ? (nck - qd + 3) / 4 : 0;   // chunks qd + 4k of this quad
+  if (mine > 0) {
+    constexpr int kDepth = 4;
+    f4_t buf[kDepth][8];
+    float2 mlb[kDepth];
+    auto fetch = [&](int k, int slot) {
+      const int64_t row = base + (int64_t)(qd + 4 * k) * p.Hq;
+      mlb[slot] = *reinterpret_cast<const float2*>(p.part_ml + row * 2);
       const f4_t* src = reinterpret_cast<const f4_t*>(p.part_o + row * kD + 8 * lam);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const f4_t a = src[8 * i], bb = src[8 * i + 1];
+        buf[slot][2 * i] = src[8 * i];
+        buf[slot][2 * i + 1] = src[8 * i + 1];
+      }
+    };
+    auto accumulate = [&](int slot) {
+      const float ref = mlb[slot].x;
+      if (ref == -INFINITY) return;                 // no valid token in the chunk
+      if (ref > M) {
+        const float r = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - ref);
+        lsum *= r;
+#pragma unroll
+        for (int k = 0; k < kElems; ++k) x[k] *= r;
+        M = ref;
+      }
+      const float sc = __builtin_amdgcn_exp2f(ref - M);
+      lsum += sc * mlb[slot].y;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          x[8 * i + j] += sc * a[j];
-          x[8 * i + 4 + j] += sc * bb[j];
+          x[8 * i + j] += sc * buf[slot][2 * i][j];
+          x[8 * i + 4 + j] += sc * buf[slot][2 * i + 1][j];
         }
+    };
+#pragma unroll
+    for (int k = 0; k < kDepth - 1; ++k)
+      if (k < mine) fetch(k, k);
+    for (int k0 = 0; k0 < mine; k0 += kDepth) {
+#pragma unroll
+      for (int k = 0; k < kDepth; ++k) {
+        const int kk = k0 + k;
+        if (kk >= mine) break;
+        if (kk + kDepth - 1 < mine) fetch(kk + kDepth - 1, (k + kDepth - 1) % kDepth);
+        accumulate(k);
       }
     }
   }
+  // merge the four quads of the row
+  const float Mv = quads_max(M);
+  const float rq = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - Mv);
+  lsum = quads_sum(lsum * rq);
+#pragma unroll
+  for (int k = 0; k < kElems; ++k) x[k] = quads_sum(x[k] * rq);
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
 #pragma unroll
   for (int k = 0; k < kElems; ++k) x[k] *= inv;
@@ -639,7 +1010,7 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(CombineParams p) {
 #pragma unroll
     for (int k = 0; k < kElems; ++k) x[k] *= cs;
   }
-  if (live) {
+  if (live && qd == 0) {
     u4_t* dst = reinterpret_cast<u4_t*>(p.out + v * kD + 8 * lam);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -673,7 +1044,7 @@ constexpr int64_t kMaxContext = INT64_C(1) << 30;
 struct Layout {
   int C;                   // tokens per chunk
   int64_t NC;              // chunks per sequence
-  size_t qprep, qconst, ml, o, total;   // byte offsets and size
+  size_t ml, o, total;     // byte offsets and size
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -688,10 +1059,6 @@ Layout make_layout(int64_t B, int32_t Hq, int32_t H, int64_t max_context) {
   L.C = C;
   L.NC = max_context > 0 ? (max_context + C - 1) / C : 1;
   size_t off = 0;
-  L.qprep = off;
-  off = align256(off + (size_t)B * H * 64 * sawkv::attn::kQWords * 4);
-  L.qconst = off;
-  off = align256(off + (size_t)B * H * 32 * 4);
   L.ml = off;
   off = align256(off + (size_t)B * L.NC * Hq * 2 * 4);
   L.o = off;
@@ -716,6 +1083,8 @@ int check_attn_sizes(int64_t B, int32_t Hq, int32_t H, int32_t D, int64_t max_co
                 (long long)max_context);
   if (B > (INT64_C(1) << 24))
     return fail(SAWKV_EUNSUPPORTED, "B = %lld too large (at most 2^24)", (long long)B);
+  if (B * Hq >= (INT64_C(1) << 33))
+    return fail(SAWKV_EUNSUPPORTED, "B * Hq too large for one launch");
   const Layout lay = make_layout(B, Hq, H, max_context);
   // grid of the chunk kernel: ceil(B * NC / 8) * 8 * H blocks
   if (((B * lay.NC + 7) / 8) * 8 * H >= (INT64_C(1) << 31))
@@ -724,13 +1093,11 @@ int check_attn_sizes(int64_t B, int32_t Hq, int32_t H, int32_t D, int64_t max_co
 }
 
 using sawkv::attn::attn_chunk_kernel;
+using sawkv::attn::attn_chunk_pair_kernel;
 using sawkv::attn::attn_combine_kernel;
-using sawkv::attn::attn_prep_kernel;
 
 int g_index(int32_t G) { return G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3; }
 
-const void* const kPrep[4] = {(void*)&attn_prep_kernel<1>, (void*)&attn_prep_kernel<2>,
-                              (void*)&attn_prep_kernel<4>, (void*)&attn_prep_kernel<8>};
 const void* const kChunk[4] = {(void*)&attn_chunk_kernel<1>, (void*)&attn_chunk_kernel<2>,
                                (void*)&attn_chunk_kernel<4>, (void*)&attn_chunk_kernel<8>};
 const void* const kCombine[5] = {(void*)&attn_combine_kernel<0>, (void*)&attn_combine_kernel<16>,
@@ -788,17 +1155,9 @@ int attention_impl(const void* q, int64_t q_stride, const void* k_codes, const v
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
-  sawkv::attn::PrepParams pp{};
-  pp.q = static_cast<const __half*>(q);
-  pp.q_stride = q_stride;
-  pp.qprep = reinterpret_cast<uint32_t*>(ws + lay.qprep);
-  pp.qconst = reinterpret_cast<float*>(ws + lay.qconst);
-  pp.H = H;
-  pp.h = h;
-  pp.rot_k = rot_mode != SAWKV_ROT_NONE;
-  pp.c_h = (float)(1.0 / sqrt((double)h));
-  pp.c_sm = (float)((double)sm_scale * 1.4426950408889634);
-  if ((st = launch64(kPrep[g_index(G)], B * H, &pp, s))) return st;
+  // four queries per head and an even head count: heads are processed in pairs
+  const bool pair = G == 4 && H % 2 == 0;
+  const int32_t groups = pair ? H / 2 : H;
 
   sawkv::attn::ChunkParams cp{};
   cp.k_codes = static_cast<const uint8_t*>(k_codes);
@@ -808,8 +1167,12 @@ int attention_impl(const void* q, int64_t q_stride, const void* k_codes, const v
   cp.block_tables = block_tables;
   cp.bt_stride = bt_stride;
   cp.context_lens = context_lens;
-  cp.qprep = pp.qprep;
-  cp.qconst = pp.qconst;
+  cp.qp.q = static_cast<const __half*>(q);
+  cp.qp.q_stride = q_stride;
+  cp.qp.h = h;
+  cp.qp.rot_k = rot_mode != SAWKV_ROT_NONE;
+  cp.qp.c_h = (float)(1.0 / sqrt((double)h));
+  cp.qp.c_sm = (float)((double)sm_scale * 1.4426950408889634);
   cp.part_o = reinterpret_cast<float*>(ws + lay.o);
   cp.part_ml = reinterpret_cast<float*>(ws + lay.ml);
   cp.N_pg = N_pg;
@@ -820,8 +1183,11 @@ int attention_impl(const void* q, int64_t q_stride, const void* k_codes, const v
   cp.C = lay.C;
   cp.max_context = (int32_t)max_context;
   cp.n_groups = (uint32_t)(B * lay.NC);
-  const int64_t chunk_blocks = ((B * lay.NC + 7) / 8) * 8 * H;
-  if (max_context > 0 && (st = launch64(kChunk[g_index(G)], chunk_blocks, &cp, s))) return st;
+  const int64_t chunk_blocks = ((B * lay.NC + 7) / 8) * 8 * groups;
+  if (max_context > 0 &&
+      (st = launch64(pair ? (const void*)&attn_chunk_pair_kernel : kChunk[g_index(G)],
+                     chunk_blocks, &cp, s)))
+    return st;
 
   sawkv::attn::CombineParams mp{};
   mp.part_o = cp.part_o;
@@ -834,7 +1200,7 @@ int attention_impl(const void* q, int64_t q_stride, const void* k_codes, const v
   mp.C = lay.C;
   mp.max_context = (int32_t)max_context;
   const int hv = rot_mode == SAWKV_ROT_KV ? (h == 16 ? 1 : h == 32 ? 2 : h == 64 ? 3 : 4) : 0;
-  if ((st = launch64(kCombine[hv], (B * Hq + 15) / 16, &mp, s))) return st;
+  if ((st = launch64(kCombine[hv], (B * Hq + 3) / 4, &mp, s))) return st;
   return ok();
 }
 
