@@ -10,6 +10,8 @@ Prints ONE JSON line. Alongside the step it times, on the same batch:
   * the naive-INT4 control (sawkv_naive_int4_append), interleaved with the
     rotated kernel, for the rotate-vs-naive ratio;
   * the read-back (sawkv_dequant_gather) of the same slots;
+  * (prefill, sweep) the uncompressed fp16 cache write and token-wise INT8
+    append / read-back, with INT8's reconstruction error;
   * the CPU oracle on a bounded sample of the same batch (a baseline only).
 Roofline: achieved HBM GB/s of the append kernel (algorithmic bytes per launch
 over the event-timed average launch) against the MI355X HBM3E peak, 8 TB/s.
@@ -39,7 +41,7 @@ METRIC = ("GB/s and tokens/s of fused Hadamard+INT4 paged append; % HBM peak; "
 HBM_PEAK_GBPS = 8000.0
 ROT_NAME = {0: "none", 1: "k", 2: "kv"}
 KERNEL_SRC = [os.path.join(ROOT, "int4_kv_cache_amd", "csrc", f)
-              for f in ("sawkv.hip", "sawkv_device.hpp")]
+              for f in ("sawkv.hip", "sawkv_append.hpp", "sawkv_device.hpp")]
 ATTN_SRC = [os.path.join(ROOT, "int4_kv_cache_amd", "csrc", f)
             for f in ("sawkv_attn.hip", "sawkv_device.hpp")]
 ATTN_METRIC = ("GB/s and decode tokens/s of attention over the paged INT4 KV cache "
@@ -120,6 +122,44 @@ def sweep_variants(S, torch, wl, kv, slots, timed, stream):
             res.append({"h": h, "rotation": rot, "append_us": round(ms * 1e3, 2),
                         "GBps": round(bytes_call / (ms * 1e-3) / 1e9, 1),
                         "mse_k": mse_gpu(torch, ko, k), "mse_v": mse_gpu(torch, vo, v)})
+    return res
+
+
+def controls(S, torch, wl, kv, slots, timed, stream, h, rot):
+    """The caches the INT4 cache is compared against, on the same batch: the
+    uncompressed fp16 paged write and token-wise INT8 (rotated as the INT4
+    run, and naive), each with its bytes per token, GB/s, and the INT8
+    reconstruction MSE."""
+    k, v = kv
+    T, H, D = k.shape
+    res = {}
+    kc = torch.empty((wl.N_pg, wl.P, H, D), dtype=torch.float16, device=k.device)
+    vc = torch.empty_like(kc)
+    fn = lambda: S.cache_append(k, v, slots, kc, vc, stream=stream)
+    for _ in range(10):
+        fn()
+    ms = float(np.median([timed(fn, 50) for _ in range(5)]))
+    b = T * (H * (2 * D * 2 + 2 * D * 2) + 8)
+    res["fp16_cache_append"] = {"us": round(ms * 1e3, 2), "bytes_per_token": b // T,
+                                "GBps": round(b / (ms * 1e-3) / 1e9, 1)}
+    del kc, vc
+    pools8 = S.alloc_int8_pools(wl.N_pg, wl.P, H, D, k.device)
+    b8 = T * (H * (2 * D * 2 + 2 * D + 2 * 2) + 8)
+    for name, r in (("int8_" + ROT_NAME[rot], ROT_NAME[rot]), ("int8_none", "none")):
+        fn = lambda: S.int8_append(k, v, slots, *pools8, h=h, rot=r, stream=stream)
+        for _ in range(10):
+            fn()
+        ms = float(np.median([timed(fn, 50) for _ in range(5)]))
+        ko, vo = S.int8_gather(*pools8, slots, h=h, rot=r, stream=stream)
+        gfn = lambda: S.int8_gather(*pools8, slots, h=h, rot=r, k_out=ko, v_out=vo,
+                                    stream=stream)
+        gms = float(np.median([timed(gfn, 50) for _ in range(3)]))
+        torch.cuda.synchronize()
+        res[name] = {"append_us": round(ms * 1e3, 2), "bytes_per_token": b8 // T,
+                     "append_GBps": round(b8 / (ms * 1e-3) / 1e9, 1),
+                     "gather_us": round(gms * 1e3, 2),
+                     "gather_GBps": round(b8 / (gms * 1e-3) / 1e9, 1),
+                     "mse_k": mse_gpu(torch, ko, k), "mse_v": mse_gpu(torch, vo, v)}
     return res
 
 
@@ -409,6 +449,8 @@ def main():
     if args.workload in ("sweep", "long", "prefill"):
         ko, vo = outs[0]
         extra["mse"] = {"k": mse_gpu(torch, ko, kvs[0][0]), "v": mse_gpu(torch, vo, kvs[0][1])}
+    if args.workload in ("prefill", "sweep"):
+        extra["controls"] = controls(S, torch, wl, kvs[0], slots, timed, stream, h, rot)
 
     # attainable-bandwidth context on this machine: a 256 MiB device copy (torch)
     cbuf = torch.empty(64 * 1024 * 1024, dtype=torch.int32, device=dev)

@@ -178,6 +178,55 @@ int sawkv_naive_int4_gather(const void* k_codes, const void* v_codes,
                             void* stream);
 
 /*
+ * Controls: the caches the INT4 cache is compared against (gist.science
+ * summary of SAW-INT4, §4 Risultati Sperimentali: accuracy and throughput
+ * against a BF16 cache; ainews.cool, the table under "技术深度解析": a uniform
+ * INT8 cache). Same tokens, slots, validation, ownership and stream behaviour
+ * as sawkv_quantize_append.
+ *
+ * sawkv_cache_append: the uncompressed paged write. k_cache, v_cache are
+ * 16-bit [N_pg][P][H][D] (fp16 or bf16: the 16-bit values are copied
+ * unchanged); cache[slot][j] = the token's row j. k or v (with its cache) may
+ * be NULL; invalid slots are skipped.
+ */
+int sawkv_cache_append(const void* k, const void* v,
+                       int64_t k_stride, int64_t v_stride,
+                       const int64_t* slot_mapping, int64_t T,
+                       int32_t H, int32_t D,
+                       void* k_cache, void* v_cache,
+                       int64_t N_pg, int32_t P,
+                       void* stream);
+
+/*
+ * sawkv_int8_append: token-wise INT8 with the INT4 path's optional rotation:
+ *   s = f16(f32(amax / 127)), q = clamp(rint_half_even(f32(y / s)), -128, 127),
+ *   s == 0 -> 0; codes int8 [N_pg][P][H][D] (one byte per channel), scales
+ *   fp16 [N_pg][P][H].
+ * sawkv_int8_gather: its read-back, f16(f32(c_h * f32(F_h(q) * s))) for a
+ *   rotated tensor (F_h(q) of the integer codes is exact), f16(q * s)
+ *   otherwise; invalid slots give zero rows. Bit-exact against that
+ *   definition.
+ */
+int sawkv_int8_append(const void* k, const void* v,
+                      int64_t k_stride, int64_t v_stride,
+                      const int64_t* slot_mapping, int64_t T,
+                      int32_t H, int32_t D,
+                      void* k_codes, void* v_codes,
+                      void* k_scales, void* v_scales,
+                      int64_t N_pg, int32_t P,
+                      int32_t h, int32_t rot_mode,
+                      void* stream);
+
+int sawkv_int8_gather(const void* k_codes, const void* v_codes,
+                      const void* k_scales, const void* v_scales,
+                      int64_t N_pg, int32_t P,
+                      const int64_t* slot_mapping, int64_t T,
+                      int32_t H, int32_t D,
+                      void* k_out, void* v_out,
+                      int32_t h, int32_t rot_mode,
+                      void* stream);
+
+/*
  * Decode attention over the paged INT4 pools: one new query token per
  * sequence attends to every cached token of its sequence. This is the consumer
  * the pages fuse dequantisation into (ainews.cool, "技术深度解析" item 3:

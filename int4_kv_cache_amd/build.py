@@ -2,8 +2,9 @@
 
     python -m int4_kv_cache_amd.build
 
-Compiles int4_kv_cache_amd/csrc/sawkv.hip (write path and read-back) and
-sawkv_attn.hip (decode attention) into int4_kv_cache_amd/libsawkv.so.
+Compiles int4_kv_cache_amd/csrc/sawkv.hip (write path and read-back),
+sawkv_attn.hip (decode attention) and sawkv_controls.hip (uncompressed cache
+write, token-wise INT8) into int4_kv_cache_amd/libsawkv.so.
 Flags: -ffp-contract=off (every float32 operation rounds on its own, as the
 bit-exact definition needs), no fast-math, denormals kept (the HIP default),
 packed-fp32 instructions disabled, MFMA accumulators in VGPRs.
@@ -15,7 +16,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", f) for f in ("sawkv.hip", "sawkv_attn.hip")]
+SRCS = [os.path.join(PKG, "csrc", f)
+        for f in ("sawkv.hip", "sawkv_attn.hip", "sawkv_controls.hip")]
 OUT = os.path.join(PKG, "libsawkv.so")
 ARCH = "gfx950"
 

@@ -17,5 +17,16 @@ int ok();
 
 bool aligned(const void* p, uintptr_t a);
 
+// Size and pointer checks shared by the append / gather style entry points
+// (write path, read-back and the controls): status SAWKV_OK or an error with
+// detail text.
+int check_geometry(int64_t T, int32_t H, int32_t D, int64_t N_pg, int32_t P, int32_t h,
+                   int32_t rot_mode, const int64_t* slots);
+int check_tensor(const char* name, const void* x, int64_t stride, const void* codes,
+                 const void* scales, int32_t H, int32_t D);
+
+// Kernel-table index of a tensor: 0 = not rotated, 1..4 = h 16/32/64/128.
+int hb_index(int32_t h, bool rot);
+
 }  // namespace host
 }  // namespace sawkv

@@ -57,6 +57,15 @@ lib.sawkv_decode_attention.argtypes = [_p, _i64, _p, _p, _p, _p, _i64, _i32, _p,
                                        _i64, _i32, _i32, _i32, _i64, ctypes.c_float, _i32, _i32,
                                        _p, _p, ctypes.c_size_t, _p]
 lib.sawkv_decode_attention.restype = ctypes.c_int
+lib.sawkv_cache_append.argtypes = [_p, _p, _i64, _i64, _p, _i64, _i32, _i32, _p, _p, _i64,
+                                   _i32, _p]
+lib.sawkv_cache_append.restype = ctypes.c_int
+lib.sawkv_int8_append.argtypes = [_p, _p, _i64, _i64, _p, _i64, _i32, _i32, _p, _p, _p, _p,
+                                  _i64, _i32, _i32, _i32, _p]
+lib.sawkv_int8_append.restype = ctypes.c_int
+lib.sawkv_int8_gather.argtypes = [_p, _p, _p, _p, _i64, _i32, _p, _i64, _i32, _i32, _p, _p, _i32,
+                                  _i32, _p]
+lib.sawkv_int8_gather.restype = ctypes.c_int
 lib.sawkv_status_string.argtypes = [ctypes.c_int]
 lib.sawkv_status_string.restype = ctypes.c_char_p
 lib.sawkv_last_error.argtypes = []
@@ -331,3 +340,91 @@ class AttentionCall:
     def __call__(self, stream=None):
         _check(lib.sawkv_decode_attention(*self._args, _stream(stream)))
         return self.out
+
+
+# ---- controls: uncompressed cache write, token-wise INT8 ----
+
+def alloc_int8_pools(N_pg, P, H, D, device="cuda"):
+    """INT8 pools: codes int8 [N_pg, P, H, D] (K, V), scales fp16 [N_pg, P, H] (K, V)."""
+    kc = torch.empty((N_pg, P, H, D), dtype=torch.int8, device=device)
+    ks = torch.empty((N_pg, P, H), dtype=torch.float16, device=device)
+    return kc, torch.empty_like(kc), ks, torch.empty_like(ks)
+
+
+def _int8_pool_geometry(codes, scales):
+    if codes.dtype != torch.int8 or codes.dim() != 4 or not codes.is_contiguous():
+        raise ValueError("INT8 codes must be contiguous int8 [N_pg, P, H, D]")
+    if scales.dtype != torch.float16 or tuple(scales.shape) != tuple(codes.shape[:3]) \
+            or not scales.is_contiguous():
+        raise ValueError("scales must be contiguous fp16 [N_pg, P, H]")
+    return codes.shape
+
+
+def cache_append(k, v, slot_mapping, k_cache, v_cache, *, stream=None):
+    """Uncompressed paged write of 16-bit K/V rows (sawkv_cache_append)."""
+    ref = k if k is not None else v
+    if ref.dtype not in (torch.float16, torch.bfloat16) or ref.dim() != 3:
+        raise ValueError("K/V must be fp16 or bf16 [T, H, D]")
+    T, H, D = ref.shape
+    strides = []
+    for x, c in ((k, k_cache), (v, v_cache)):
+        if x is None:
+            strides.append(0)
+            continue
+        if x.dtype != ref.dtype or x.shape != ref.shape or x.stride(2) != 1 \
+                or (H > 1 and x.stride(1) != D):
+            raise ValueError("K/V must share shape and dtype, unit channel stride, head stride D")
+        if c.dtype != ref.dtype or c.dim() != 4 or tuple(c.shape[2:]) != (H, D) \
+                or not c.is_contiguous():
+            raise ValueError("caches must be contiguous [N_pg, P, H, D] of the K/V dtype")
+        strides.append(x.stride(0))
+    cache = k_cache if k is not None else v_cache
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must be int64 [T]")
+    _check(lib.sawkv_cache_append(_addr(k), _addr(v), strides[0], strides[1],
+                                  _addr(slot_mapping), T, H, D,
+                                  _addr(k_cache) if k is not None else None,
+                                  _addr(v_cache) if v is not None else None,
+                                  cache.shape[0], cache.shape[1], _stream(stream)))
+
+
+def int8_append(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, *, h=128, rot="none",
+                stream=None):
+    """Token-wise INT8 append (sawkv_int8_append)."""
+    ref = k if k is not None else v
+    T, H, D, _ = _kv_geometry(ref)
+    ks_ = _kv_geometry(k)[3] if k is not None else 0
+    vs_ = _kv_geometry(v)[3] if v is not None else 0
+    pool = _int8_pool_geometry(k_codes, k_scales) if k is not None else \
+        _int8_pool_geometry(v_codes, v_scales)
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must be int64 [T]")
+    _check(lib.sawkv_int8_append(
+        _addr(k), _addr(v), ks_, vs_, _addr(slot_mapping), T, H, D,
+        _addr(k_codes) if k is not None else None, _addr(v_codes) if v is not None else None,
+        _addr(k_scales) if k is not None else None, _addr(v_scales) if v is not None else None,
+        pool[0], pool[1], h, _rot(rot), _stream(stream)))
+
+
+def int8_gather(k_codes, v_codes, k_scales, v_scales, slot_mapping, *, h=128, rot="none",
+                k_out=None, v_out=None, want_k=True, want_v=True, stream=None):
+    """INT8 read-back (sawkv_int8_gather). Returns (k_out, v_out)."""
+    pool = _int8_pool_geometry(k_codes, k_scales) if want_k else \
+        _int8_pool_geometry(v_codes, v_scales)
+    N_pg, P, H, D = pool
+    T = slot_mapping.numel()
+    if slot_mapping.dtype != torch.int64:
+        raise ValueError("slot_mapping must be int64 [T]")
+    dev = (k_codes if want_k else v_codes).device
+    if want_k and k_out is None:
+        k_out = torch.empty((T, H, D), dtype=torch.float16, device=dev)
+    if want_v and v_out is None:
+        v_out = torch.empty((T, H, D), dtype=torch.float16, device=dev)
+    k_out = k_out if want_k else None
+    v_out = v_out if want_v else None
+    _check(lib.sawkv_int8_gather(
+        _addr(k_codes) if want_k else None, _addr(v_codes) if want_v else None,
+        _addr(k_scales) if want_k else None, _addr(v_scales) if want_v else None,
+        N_pg, P, _addr(slot_mapping), T, H, D, _addr(k_out), _addr(v_out), h, _rot(rot),
+        _stream(stream)))
+    return k_out, v_out

@@ -278,3 +278,64 @@ def test_attention_workspace_size(lib):
     # a workspace one byte short of the reported size is refused
     assert attn(lib, wsb=n - 1) == EINVAL
     assert b"workspace" in lib.sawkv_last_error()
+
+
+# ---- controls: uncompressed cache write and token-wise INT8 (validation only) ----
+
+def ctl(lib, name, **kw):
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    if name == "cache":
+        f = lib.sawkv_cache_append
+        f.argtypes = [p, p, i64, i64, p, i64, i32, i32, p, p, i64, i32, p]
+        a = dict(k=K, v=V, ks=1024, vs=1024, slots=S, T=64, H=8, D=128, kc=KC, vc=VC, npg=16,
+                 P=16)
+        a.update(kw)
+        return f(a["k"], a["v"], a["ks"], a["vs"], a["slots"], a["T"], a["H"], a["D"], a["kc"],
+                 a["vc"], a["npg"], a["P"], None)
+    if name == "append8":
+        f = lib.sawkv_int8_append
+        f.argtypes = [p, p, i64, i64, p, i64, i32, i32, p, p, p, p, i64, i32, i32, i32, p]
+        a = dict(k=K, v=V, ks=1024, vs=1024, slots=S, T=64, H=8, D=128, kc=KC, vc=VC, kss=KS,
+                 vss=VS, npg=16, P=16, h=128, rot=2)
+        a.update(kw)
+        return f(a["k"], a["v"], a["ks"], a["vs"], a["slots"], a["T"], a["H"], a["D"], a["kc"],
+                 a["vc"], a["kss"], a["vss"], a["npg"], a["P"], a["h"], a["rot"], None)
+    f = lib.sawkv_int8_gather
+    f.argtypes = [p, p, p, p, i64, i32, p, i64, i32, i32, p, p, i32, i32, p]
+    a = dict(kc=KC, vc=VC, kss=KS, vss=VS, npg=16, P=16, slots=S, T=64, H=8, D=128, ko=K, vo=V,
+             h=128, rot=2)
+    a.update(kw)
+    return f(a["kc"], a["vc"], a["kss"], a["vss"], a["npg"], a["P"], a["slots"], a["T"], a["H"],
+             a["D"], a["ko"], a["vo"], a["h"], a["rot"], None)
+
+
+@pytest.mark.parametrize("name", ["cache", "append8", "gather8"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), EINVAL),
+    (dict(H=0), EINVAL),
+    (dict(D=64), EUNSUPPORTED),
+    (dict(npg=0), EINVAL),
+    (dict(slots=None), EINVAL),
+    (dict(slots=S + 4), EALIGN),
+])
+def test_control_validation(lib, name, kw, status):
+    assert ctl(lib, name, **kw) == status
+    assert lib.sawkv_last_error() != b""
+
+
+def test_control_specific_validation(lib):
+    assert ctl(lib, "cache", k=None, v=None) == EINVAL
+    assert ctl(lib, "cache", k=K + 8) == EALIGN
+    assert ctl(lib, "cache", ks=1000) == EINVAL
+    assert ctl(lib, "cache", kc=None) == EINVAL
+    assert ctl(lib, "append8", h=48) == EUNSUPPORTED
+    assert ctl(lib, "append8", rot=5) == EINVAL
+    assert ctl(lib, "append8", vss=VS + 2) == EALIGN
+    assert ctl(lib, "gather8", ko=None, vo=None) == EINVAL
+    assert ctl(lib, "gather8", kc=None) == EINVAL
+    # T == 0 reads no pointer
+    assert ctl(lib, "cache", T=0, k=None, v=None, kc=None, vc=None, slots=None) == OK
+    assert ctl(lib, "append8", T=0, k=None, v=None, kc=None, vc=None, kss=None, vss=None,
+               slots=None) == OK
+    assert ctl(lib, "gather8", T=0, ko=None, vo=None, kc=None, vc=None, kss=None, vss=None,
+               slots=None) == OK

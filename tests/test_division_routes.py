@@ -2,7 +2,8 @@
 checks those routes in exact rational arithmetic on the CPU (no GPU, no oracle):
 
   * amax / 7:  q0 = RN(a * r7), e = RN(a - 7 q0) (exact, one fma),
-               RN(q0 + e * r7) with r7 = RN(1/7)          (Markstein's correction)
+               RN(q0 + e * r7) with r7 = RN(1/7)          (Markstein's correction);
+               the same with 127 for the INT8 control's scale
   * 1 / s for an fp16-valued s: r0 = any float32 within one ulp of 1/s (the
                hardware reciprocal), e = RN(1 - s r0) (exact), RN(r0 + r0 e)
   * y / s:     q0 = RN(y * r), e = RN(y - s q0) (exact), RN(q0 + e r), r = RN(1/s)
@@ -19,6 +20,7 @@ import pytest
 from tests.exact_fp import F16, rn
 
 R7 = Fraction(0x124925 | 0x800000, 1 << 26)      # float32 0x3E124925
+R127 = Fraction(0x010204 | 0x800000, 1 << 30)    # float32 0x3C010204
 
 
 def fma(a, b, c):
@@ -37,6 +39,7 @@ def ulp32(x):
 
 def test_r7_is_rn_of_one_seventh():
     assert R7 == rn(Fraction(1, 7))
+    assert R127 == rn(Fraction(1, 127))
 
 
 def div7_route(a):
@@ -57,6 +60,25 @@ def test_div7_route_is_correctly_rounded():
             cases.append(Fraction((1 << 23) | m) * Fraction(2) ** (e - 23))
     for a in cases:
         assert div7_route(a) == rn(a / 7), a
+
+
+def div127_route(a):
+    q0 = rn(a * R127)
+    e = fma(-q0, Fraction(127), a)
+    assert e == a - 127 * q0
+    return fma(e, R127, q0)
+
+
+def test_div127_route_is_correctly_rounded():
+    """amax / 127 for the INT8 control's scale, same sweep as for / 7."""
+    rng = np.random.default_rng(5)
+    cases = [Fraction(0), Fraction(127), Fraction(1, 1 << 20)]
+    for e in range(-27, 21):
+        for m in list(range(0, 64)) + list(range((1 << 23) - 64, 1 << 23)) + \
+                [int(v) for v in rng.integers(0, 1 << 23, 64)]:
+            cases.append(Fraction((1 << 23) | m) * Fraction(2) ** (e - 23))
+    for a in cases:
+        assert div127_route(a) == rn(a / 127), a
 
 
 def fp16_values():
