@@ -31,18 +31,51 @@ namespace sawkv {
 // append: fp16 K/V -> rotate -> token-wise INT4 -> paged pool
 // ---------------------------------------------------------------------------
 
+// Packs 8 biased codes (q + 8 in the low 4 bits of each word, constant bits
+// above bit 21) into one word of nibbles: byte b = q_{2b} | q_{2b+1} << 4.
+__device__ __forceinline__ uint32_t pack_low(const uint32_t* w) {
+  const uint32_t p01 = shl4_or(w[1], w[0]);   // byte 0 = nibbles 0,1; byte 1 = 0
+  const uint32_t p23 = shl4_or(w[3], w[2]);
+  const uint32_t p45 = shl4_or(w[5], w[4]);
+  const uint32_t p67 = shl4_or(w[7], w[6]);
+  const uint32_t lo = shl8_or(p23, p01);      // bytes 0-1 valid
+  const uint32_t hi = shl8_or(p67, p45);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u) ^ 0x88888888u;
+}
+
+// The same from codes held in byte 2 of each word (bits 16-19, bits 20-23 zero).
+__device__ __forceinline__ uint32_t pack_byte2(const uint32_t* w) {
+  const uint32_t e0 = __builtin_amdgcn_perm(w[4], w[0], 0x0C060C02u);   // c0, 0, c4, 0
+  const uint32_t o0 = __builtin_amdgcn_perm(w[5], w[1], 0x0C060C02u);   // c1, 0, c5, 0
+  const uint32_t e1 = __builtin_amdgcn_perm(w[6], w[2], 0x0C060C02u);   // c2, 0, c6, 0
+  const uint32_t o1 = __builtin_amdgcn_perm(w[7], w[3], 0x0C060C02u);   // c3, 0, c7, 0
+  const uint32_t y0 = shl4_or(o0, e0);   // c0|c1<<4, 0, c4|c5<<4, 0
+  const uint32_t y1 = shl4_or(o1, e1);   // c2|c3<<4, 0, c6|c7<<4, 0
+  return shl8_or(y1, y0) ^ 0x88888888u;
+}
+
+// min of the low 16 bits of three words
+__device__ __forceinline__ uint32_t min3_lo16(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t d;
+  asm("v_min3_u16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
 template <int HB>
 __device__ __forceinline__ void quantize_store(const AppendTensor& A, const AppendParams& p,
                                                const Fetched& f, int lam) {
-  float y[kElems];
-  load_transform<HB>(f.raw, y, lam);
+  float u[kElems];
+  const float csg = load_rotate<HB>(f.raw, u, lam);   // y = f32(u * csg)
 
-  // token-wise scale: amax over the 128 channels of the vector (4 lanes)
-  float m = 0.0f;
+  // token-wise scale: amax over the 128 channels of the vector (4 lanes).
+  // max |y| = f32(c_h * max |u|): rounding is monotonic and the sign exact.
+  float mu = 0.0f;
 #pragma unroll
-  for (int k = 0; k < kElems; ++k) m = fmaxf(m, fabsf(y[k]));
-  m = fmaxf(m, quad_xor1(m));
-  m = fmaxf(m, quad_xor2(m));
+  for (int k = 0; k < kElems; ++k) mu = fmaxf(mu, fabsf(u[k]));
+  mu = fmaxf(mu, quad_xor1(mu));
+  mu = fmaxf(mu, quad_xor2(mu));
+  float m = mu;
+  if constexpr (HB != 0) m = mu * c_h<HB>();
   // s32 = RN(amax / 7) by Markstein's correction with r7 = RN(1/7); the fma
   // residual is exact, so the corrected quotient is the IEEE one
   const float r7 = __builtin_bit_cast(float, 0x3E124925u);
@@ -56,38 +89,52 @@ __device__ __forceinline__ void quantize_store(const AppendTensor& A, const Appe
   // float32 midpoint, while the corrected value is within 2^-46 of 1/sf
   const float r0 = __builtin_amdgcn_rcpf(sf);
   const float r = sf > 0.0f ? __builtin_fmaf(r0, __builtin_fmaf(-sf, r0, 1.0f), r0) : 0.0f;
-  // clamp to [-8, 7] can bite only for a saturated or an f16-subnormal scale
-  const bool need_clamp = (s32 > 65504.0f) || (sf < 6.103515625e-05f);
+  // the clamp to [-8, 7] can bite only for a saturated or an f16-subnormal scale
+  const bool need_clamp = (s32 > 65504.0f) || (sf > 0.0f && sf < 6.103515625e-05f);
 
-  // q = rint(f32(y / s)): Markstein's correction of y * RN(1/s) gives the
-  // correctly rounded quotient (residual by fma, exact); adding 1.5*2^23 + 8
-  // then rounds to an integer half-to-even and leaves q + 8 in the low bits.
-  uint32_t u[kElems];
-#pragma unroll
-  for (int k = 0; k < kElems; ++k) {
-    const float q0 = y[k] * r;
-    const float e = __builtin_fmaf(-q0, sf, y[k]);
-    const float q1 = __builtin_fmaf(e, r, q0);
-    u[k] = __builtin_bit_cast(uint32_t, q1 + 12582920.0f);
-  }
-  if (__any(need_clamp)) {
-#pragma unroll
-    for (int k = 0; k < kElems; ++k) u[k] = min(max(u[k], 0x4B400000u), 0x4B40000Fu);
-  }
-
-  // pack: byte b of chunk i = (q_{2b} & 15) | (q_{2b+1} & 15) << 4; the
-  // nibbles hold q + 8 until the final xor with 0x8 per nibble
+  // Fast route, one fma per channel: t = u * RN(c_h r) + (136.5 + 2^-16),
+  // rounded once to the 2^-16 grid of [128, 256), so byte 2 of t's bits is
+  // floor(t - 128) = q + 8. u * RN(c_h r) is within 2^-19 of the exact
+  // quotient f32(y / s) (|q| < 7.004, four float32 roundings), so the code is
+  // rint(f32(y / s)) + 8 unless a half-integer lies within that distance;
+  // then t lands on or one step above an integer, its low 16 bits are 0 or 1,
+  // and the wave takes the exact route below. A zero scale gives r = 0, t =
+  // 136.5 + 2^-16 and code 0.
+  const float cr = HB != 0 ? r * csg : r;
+  const float kT = __builtin_bit_cast(float, 0x43088001u);     // 136.5 + 2^-16
+  uint32_t near = 0xFFFFu;
   uint32_t d[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t* w = u + 8 * i;
-    const uint32_t p01 = shl4_or(w[1], w[0]);   // byte 0 = nibbles 0,1; byte 1 = 0
-    const uint32_t p23 = shl4_or(w[3], w[2]);
-    const uint32_t p45 = shl4_or(w[5], w[4]);
-    const uint32_t p67 = shl4_or(w[7], w[6]);
-    const uint32_t lo = shl8_or(p23, p01);      // bytes 0-1 valid
-    const uint32_t hi = shl8_or(p67, p45);
-    d[i] = __builtin_amdgcn_perm(hi, lo, 0x05040100u) ^ 0x88888888u;
+    uint32_t t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      t[j] = __builtin_bit_cast(uint32_t, __builtin_fmaf(u[8 * i + j], cr, kT));
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) near = min3_lo16(near, t[j], t[j + 1]);
+    d[i] = pack_byte2(t);
+  }
+
+  if (__any(need_clamp || (near & 0xFFFFu) <= 1u)) {
+    uint32_t w[kElems];
+    // Exact route: y = f32(u * csg); q = rint(f32(y / s)) from Markstein's
+    // correction of y * RN(1/s) (residual by fma, exact), which is the
+    // correctly rounded quotient; adding 1.5*2^23 + 8 rounds to an integer
+    // half-to-even and leaves q + 8 in the low bits.
+#pragma unroll
+    for (int k = 0; k < kElems; ++k) {
+      const float y = HB != 0 ? u[k] * csg : u[k];
+      const float q0 = y * r;
+      const float e = __builtin_fmaf(-q0, sf, y);
+      const float q1 = __builtin_fmaf(e, r, q0);
+      w[k] = __builtin_bit_cast(uint32_t, q1 + 12582920.0f);
+    }
+    if (__any(need_clamp)) {
+#pragma unroll
+      for (int k = 0; k < kElems; ++k) w[k] = min(max(w[k], 0x4B400000u), 0x4B40000Fu);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = pack_low(w + 8 * i);
   }
 
   if (f.in_range && f.slot >= 0 && f.slot < p.n_slots) {

@@ -28,11 +28,11 @@ struct AppendParams {
   uint32_t h_magic;      // ceil(2^20 / H): n / H = (n * h_magic) >> 20 for n < 2^9
 };
 
-// y = float32 input, or f32(c_h * F_h(x)) with the lane's sign removed.
-// HB == 0: no rotation (naive INT4).
+// u = float32 input (HB == 0, naive INT4), or F_h(x) up to the lane's sign;
+// returns csg with y = f32(u * csg) the rotated vector f32(c_h * F_h(x))
+// (csg = +-c_h, exact sign), or 1 for HB == 0.
 template <int HB>
-__device__ __forceinline__ void load_transform(const uint4 (&raw)[4], float (&y)[kElems],
-                                               int lam) {
+__device__ __forceinline__ float load_rotate(const uint4 (&raw)[4], float (&u)[kElems], int lam) {
   if constexpr (HB == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -40,10 +40,11 @@ __device__ __forceinline__ void load_transform(const uint4 (&raw)[4], float (&y)
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const __half2 hv = __builtin_bit_cast(__half2, w[m]);
-        y[8 * i + 2 * m] = __low2float(hv);
-        y[8 * i + 2 * m + 1] = __high2float(hv);
+        u[8 * i + 2 * m] = __low2float(hv);
+        u[8 * i + 2 * m + 1] = __high2float(hv);
       }
     }
+    return 1.0f;
   } else {
     // stride-1 butterflies straight from the fp16 pairs: fma(b, 1, a) = f32(a + b)
     // and fma(b, -1, a) = f32(a - b), one mixed-precision fma each
@@ -55,12 +56,21 @@ __device__ __forceinline__ void load_transform(const uint4 (&raw)[4], float (&y)
       for (int m = 0; m < 4; ++m) {
         const __half2 hv = __builtin_bit_cast(__half2, w[m]);
         const float a = __low2float(hv), b = __high2float(hv);
-        y[8 * i + 2 * m] = __builtin_fmaf(b, one, a);
-        y[8 * i + 2 * m + 1] = __builtin_fmaf(b, -one, a);
+        u[8 * i + 2 * m] = __builtin_fmaf(b, one, a);
+        u[8 * i + 2 * m + 1] = __builtin_fmaf(b, -one, a);
       }
     }
-    const float sgn = fwht_rest<HB>(y, lam);
-    const float csg = c_h<HB>() * sgn;
+    return c_h<HB>() * fwht_rest<HB>(u, lam);
+  }
+}
+
+// y = float32 input, or f32(c_h * F_h(x)) with the lane's sign removed.
+// HB == 0: no rotation (naive INT4).
+template <int HB>
+__device__ __forceinline__ void load_transform(const uint4 (&raw)[4], float (&y)[kElems],
+                                               int lam) {
+  const float csg = load_rotate<HB>(raw, y, lam);
+  if constexpr (HB != 0) {
 #pragma unroll
     for (int k = 0; k < kElems; ++k) y[k] = y[k] * csg;
   }

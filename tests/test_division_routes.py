@@ -116,3 +116,83 @@ def test_quotient_route_near_half_integers():
                 e = fma(-q0, s, y)
                 assert e == y - s * q0
                 assert fma(e, r, q0) == rn(y / s), (s, y)
+
+
+# Single-fma code route of the INT4 append (fast path): t = RN(u * RN(c r) + kT)
+# with kT = 136.5 + 2^-16, so that t lies in [128, 256) on the 2^-16 grid; the
+# code is floor(t - 128) - 8 (byte 2 of t's bits) unless the low 16 bits of t
+# are 0 or 1, which sends the wave to the exact route above. u is the
+# un-normalised transform value, y = RN(c u) the rotated value (c = 1 without
+# rotation), r = RN(1/s).
+KT = Fraction(273, 2) + Fraction(1, 1 << 16)
+C_H = {1: Fraction(1), 16: Fraction(1, 4), 64: Fraction(1, 8),
+       32: Fraction(0x3504F3 | 0x800000, 1 << 26),        # float32 0x3E3504F3
+       128: Fraction(0x3504F3 | 0x800000, 1 << 27)}       # float32 0x3DB504F3
+
+
+def rint_even(x):
+    n = math.floor(x)
+    r = x - n
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return n
+
+
+def code_route(u, cr):
+    t = rn(u * cr + KT)
+    assert 128 <= t < 256
+    n = (t - 128) * (1 << 16)
+    assert n.denominator == 1
+    n = n.numerator
+    return (n >> 16) - 8, (n & 0xFFFF) <= 1
+
+
+def test_c_h_constants_are_rn_of_inverse_sqrt():
+    for h in (32, 128):
+        c = C_H[h]
+        assert rn(c) == c
+        lo, hi = c - ulp32(c) / 2, c + ulp32(c) / 2
+        assert lo * lo * h < 1 < hi * hi * h
+
+
+def test_single_fma_route_flags_every_misrounding():
+    """For fp16 scales s and rotated values y within a few ulps of every
+    half-integer multiple of s (and random ones), every code the fast route
+    does not flag equals rint(RN(y / s)); near-ties are flagged, random values
+    rarely are."""
+    rng = np.random.default_rng(7)
+    scales = fp16_values()
+    normal = [s for s in scales if s >= Fraction(1, 1 << 14)]
+    pick = [normal[i] for i in rng.choice(len(normal), 24, replace=False)]
+    pick += [Fraction(1, 1 << 14), Fraction(65504), Fraction(1), Fraction(3, 1 << 12)]
+    flagged_near = total_near = flagged_rand = total_rand = 0
+    for s in pick:
+        r = rn(1 / s)
+        for h, c in C_H.items():
+            cr = rn(c * r)
+            cases = []
+            for k in range(-8, 8):
+                target = rn(Fraction(2 * k + 1, 2) * s)
+                for d in (-2, -1, 0, 1, 2):
+                    y = target + d * ulp32(target)
+                    u0 = rn(y / c)
+                    for du in (-1, 0, 1):
+                        cases.append((u0 + du * ulp32(u0), True))
+            for v in rng.uniform(-7.0, 7.0, 40):
+                cases.append((rn(Fraction(float(v)) * s / c), False))
+            for u, near in cases:
+                y = rn(c * u)
+                if abs(y / s) > Fraction(7004, 1000):
+                    continue
+                want = max(-8, min(7, rint_even(rn(y / s))))
+                code, flag = code_route(u, cr)
+                if not flag:
+                    assert code == want, (s, h, u)
+                if near:
+                    total_near += 1
+                    flagged_near += flag
+                else:
+                    total_rand += 1
+                    flagged_rand += flag
+    assert flagged_near > total_near // 4
+    assert flagged_rand * 100 < total_rand

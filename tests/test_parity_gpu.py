@@ -215,6 +215,42 @@ def test_edge_values(env, h, rot):
     run_case(env, k, v, slots, 13, 16, h, rot, what=f"edge h={h} rot={rot}")
 
 
+def _rotated_ties(rng, T, H, h, mix):
+    """fp16 vectors whose rotation F_h(x) / sqrt(h) is exactly y, with y's
+    entries half-integer multiples of 2^e and one entry 7 * 2^e: the scale is
+    2^e and every quotient y / s is an exact tie (h = 16, 64: c_h a power of
+    two, so all of it is exact). Every `mix`-th vector is random instead, so
+    flagged and unflagged vectors share waves."""
+    y = (rng.integers(-7, 7, size=(T, H, 128)) + 0.5).astype(np.float64)
+    y[..., 5] = 7.0 * np.where(rng.random((T, H)) < 0.5, 1, -1)
+    y *= 2.0 ** rng.integers(-6, 4, size=(T, H, 1))
+    blk = np.kron(np.eye(128 // h), _sylvester(h))
+    x = (y @ blk) / np.sqrt(h)                      # R = F_h / sqrt(h) is its own inverse
+    x16 = x.astype(np.float16)
+    assert np.array_equal(x16.astype(np.float64), x)
+    x16[::mix] = rng.standard_normal((len(x16[::mix]), H, 128)).astype(np.float16)
+    return x16
+
+
+def _sylvester(h):
+    m = np.ones((1, 1))
+    while m.shape[0] < h:
+        m = np.block([[m, m], [m, -m]])
+    return m
+
+
+@pytest.mark.parametrize("h", [16, 64])
+def test_rotated_exact_ties(env, h):
+    """Exact ties after rotation: the waves holding them take the exact route
+    and round half to even, like the oracle."""
+    rng = np.random.default_rng(90 + h)
+    T, H = 96, 4
+    k = _rotated_ties(rng, T, H, h, mix=7)
+    v = _rotated_ties(rng, T, H, h, mix=3)
+    slots = rng.permutation(T).astype(np.int64)
+    run_case(env, k, v, slots, 6, 16, h, O.ROT_KV, what=f"rotated ties h={h}")
+
+
 def test_single_tensor_calls(env):
     rng = np.random.default_rng(44)
     T, H = 100, 8
