@@ -162,56 +162,93 @@ __device__ __forceinline__ bool column_hi(int n) {
 // sum of the query's effective multipliers, cinit) and the log2-unit scale F.
 // The wave's queries are those of head group `hg` of sequence b: one KV head,
 // or a pair of KV heads (PAIR). xs: NQ x 128 floats of LDS. One wave.
+//
+// Query g of the wave is held by LQ = 64 / NQ consecutive lanes, CPL = 2 NQ
+// contiguous channels per lane, so the Walsh-Hadamard stages of stride < CPL
+// are in-lane and the others pair lane j of the query with lane j ^ (s / CPL):
+// the lower lane takes fma(a, 1, b) = f32(a + b), the upper fma(b, -1, a) =
+// f32(a - b), the same butterflies in the same order as the definition. The
+// query's reductions run over its own LQ lanes.
 template <int G, bool PAIR>
 __device__ __forceinline__ void prepare_query(const QueryParams& p, int64_t b, int hg, int lane,
                                               float (*xs)[kD], u4_t (&bq)[4], float& cinit_n,
                                               float& F_n) {
   constexpr int NQ = PAIR ? 2 * G : G;          // queries of the wave
   static_assert(!PAIR || G == 4, "head pairs are laid out for 4 queries per head");
-  const int h = hg;
+  constexpr int LQ = 64 / NQ;                   // lanes per query
+  constexpr int CPL = kD / LQ;                  // channels per lane
+  const int g = lane / LQ, j = lane % LQ;
 
+  float x[CPL];
+  {
+    // rows are 16-byte aligned (q and q_stride); CPL halves from channel j * CPL
+    const __half* row = p.q + b * p.q_stride + (int64_t)(hg * NQ + g) * kD + j * CPL;
+    if constexpr (CPL >= 8) {
 #pragma unroll
-  for (int g = 0; g < NQ; ++g) {
-    const __half* row = p.q + b * p.q_stride + (int64_t)(h * NQ + g) * kD;
-    xs[g][2 * lane] = __half2float(row[2 * lane]);
-    xs[g][2 * lane + 1] = __half2float(row[2 * lane + 1]);
-  }
-  __syncthreads();
-  if (p.rot_k) {
-    // Walsh-Hadamard butterflies within blocks of h channels; lane owns one
-    // pair (i, i + s) per query and stage.
-    for (int s = 1; s < p.h; s <<= 1) {
-      const int i = (lane / s) * 2 * s + (lane % s);
+      for (int c = 0; c < CPL / 8; ++c) {
+        const uint4 w = reinterpret_cast<const uint4*>(row)[c];
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-      for (int g = 0; g < NQ; ++g) {
-        const float a = xs[g][i], c = xs[g][i + s];
-        xs[g][i] = a + c;
-        xs[g][i + s] = a - c;
+        for (int m = 0; m < 4; ++m) {
+          const __half2 hv = __builtin_bit_cast(__half2, ws[m]);
+          x[8 * c + 2 * m] = __low2float(hv);
+          x[8 * c + 2 * m + 1] = __high2float(hv);
+        }
       }
-      __syncthreads();
+    } else {
+#pragma unroll
+      for (int m = 0; m < CPL / 2; ++m) {
+        const __half2 hv = reinterpret_cast<const __half2*>(row)[m];
+        x[2 * m] = __low2float(hv);
+        x[2 * m + 1] = __high2float(hv);
+      }
+    }
+  }
+  if (p.rot_k) {
+#pragma unroll
+    for (int s = 1; s < CPL; s <<= 1) {
+      if (s < p.h) {
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          if ((e & s) == 0) {
+            const float a = x[e], c = x[e + s];
+            x[e] = a + c;
+            x[e + s] = a - c;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int s = CPL; s < kD; s <<= 1) {
+      if (s < p.h) {
+        const int m = s / CPL;
+        const float sg = (j & m) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          const float xp = __shfl_xor(x[e], m);
+          x[e] = __builtin_fmaf(x[e], sg, xp);
+        }
+      }
     }
   }
   const float mul = p.rot_k ? p.c_h : 1.0f;
 
-  // all queries' reductions side by side (independent shuffle chains)
-  float v0[NQ], v1[NQ], amax[NQ];
+  float v[CPL];
+  float amax = 0.0f;
 #pragma unroll
-  for (int g = 0; g < NQ; ++g) {
-    v0[g] = xs[g][2 * lane] * mul * p.c_sm;
-    v1[g] = xs[g][2 * lane + 1] * mul * p.c_sm;
-    amax[g] = fmaxf(fabsf(v0[g]), fabsf(v1[g]));
+  for (int e = 0; e < CPL; ++e) {
+    v[e] = x[e] * mul * p.c_sm;
+    amax = fmaxf(amax, fabsf(v[e]));
   }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1)
+  for (int o = LQ / 2; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  int ex = 0;
+  if (amax > 0.0f) frexpf(amax, &ex);               // amax in [2^(ex-1), 2^ex)
+  const int sigma = amax > 0.0f ? 14 - ex : 0;      // max |Q| in [2^13, 2^14)
+  float msum = 0.0f;
 #pragma unroll
-    for (int g = 0; g < NQ; ++g) amax[g] = fmaxf(amax[g], __shfl_xor(amax[g], o));
-  float sig_scale[NQ], cinit[NQ], msum[NQ];
-#pragma unroll
-  for (int g = 0; g < NQ; ++g) {
-    int e = 0;
-    if (amax[g] > 0.0f) frexpf(amax[g], &e);         // amax in [2^(e-1), 2^e)
-    const int sigma = amax[g] > 0.0f ? 14 - e : 0;   // max |Q| in [2^13, 2^14)
-    const float Q0 = ldexpf(v0[g], sigma), Q1 = ldexpf(v1[g], sigma);
+  for (int e = 0; e < CPL; e += 2) {
+    const float Q0 = ldexpf(v[e], sigma), Q1 = ldexpf(v[e + 1], sigma);
     // effective multiplier of u: (hi + lo) of Q (even channel) and of Q / 16
     // times 16 (odd channel)
     const _Float16 h0 = (_Float16)Q0;
@@ -219,17 +256,14 @@ __device__ __forceinline__ void prepare_query(const QueryParams& p, int64_t b, i
     const float q16 = Q1 * 0.0625f;
     const _Float16 h1 = (_Float16)q16;
     const _Float16 l1 = (_Float16)(q16 - (float)h1);
-    msum[g] = ((float)h0 + (float)l0) + 16.0f * ((float)h1 + (float)l1);
-    sig_scale[g] = ldexpf(1.0f, 24 - sigma);
-    xs[g][2 * lane] = Q0;                      // each lane rewrites its own two channels
-    xs[g][2 * lane + 1] = q16;
+    msum += ((float)h0 + (float)l0) + 16.0f * ((float)h1 + (float)l1);
+    xs[g][j * CPL + e] = Q0;
+    xs[g][j * CPL + e + 1] = q16;
   }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1)
-#pragma unroll
-    for (int g = 0; g < NQ; ++g) msum[g] += __shfl_xor(msum[g], o);
-#pragma unroll
-  for (int g = 0; g < NQ; ++g) cinit[g] = -8.0f * ldexpf(msum[g], -24);
+  for (int o = LQ / 2; o >= 1; o >>= 1) msum += __shfl_xor(msum, o);
+  const float cinit_g = -8.0f * ldexpf(msum, -24);
+  const float sig_g = ldexpf(1.0f, 24 - sigma);
   __syncthreads();
 
   const int gl = lane >> 4, n = lane & 15;
@@ -258,15 +292,14 @@ __device__ __forceinline__ void prepare_query(const QueryParams& p, int64_t b, i
 #pragma unroll
   for (int k = 0; k < 4; ++k)
     bq[k] = u4_t{words[4 * k], words[4 * k + 1], words[4 * k + 2], words[4 * k + 3]};
-  float ci = 0.0f, f = 0.0f;
   {
     const int qi = column_query<G, PAIR>(n);
-#pragma unroll
-    for (int g = 0; g < NQ; ++g)
-      if (qi == g && column_hi<G, PAIR>(n)) { ci = cinit[g]; f = sig_scale[g]; }
+    const int src = (qi >= 0 ? qi : 0) * LQ;
+    const float ci = __shfl(cinit_g, src), f = __shfl(sig_g, src);
+    const bool take = qi >= 0 && column_hi<G, PAIR>(n);
+    cinit_n = take ? ci : 0.0f;
+    F_n = take ? f : 0.0f;
   }
-  cinit_n = ci;
-  F_n = f;
   __syncthreads();                 // xs is reused by the caller's next query group
 }
 
@@ -1055,7 +1088,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 Layout make_layout(int64_t B, int32_t Hq, int32_t H, int64_t max_context) {
   Layout L{};
   int C = 512;
-  while (C > 64 && B * H * ((max_context + C - 1) / C) < 8192) C >>= 1;
+  while (C > 128 && B * H * ((max_context + C - 1) / C) < 8192) C >>= 1;
   L.C = C;
   L.NC = max_context > 0 ? (max_context + C - 1) / C : 1;
   size_t off = 0;
