@@ -2,6 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
     python bench.py --workload attn     (decode attention over the INT4 pool)
+    python bench.py --workload concurrency  (rotated vs naive INT4 across 1..256
+                                             concurrent decodes)
 
 One step = one sawkv_quantize_append call over the workload's batch (rotate,
 token-wise INT4, pack, scatter into the paged pool: the whole write path).
@@ -325,13 +327,111 @@ def bench_attention(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_concurrency(args):
+    """The pages' serving claim, measured on this path: rotated INT4 against
+    plain (naive) INT4 across concurrency levels. Per decode step at
+    concurrency c: the 36 layers' appends of c new tokens in one launch
+    (decode recipe, K-only rotation), and decode attention of the c sequences
+    over their cached contexts (attn recipe, first c sequences), timed on one
+    layer's pool; the step estimate is append + 36 x attention."""
+    import torch
+    from int4_kv_cache_amd import sawkv as S
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    wl = W.WORKLOADS["decode"]
+    layers = wl.layers
+    print(f"[bench] generating decode + attn inputs", file=sys.stderr, flush=True)
+    slots = torch.from_numpy(W.slot_mapping(wl)).to(dev)
+    kvs = []
+    for layer in range(layers):
+        k, v = W.kv(wl, layer)
+        kvs.append((torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)))
+    pools = [S.alloc_pools(wl.N_pg, wl.P, wl.H, wl.D, dev) for _ in range(layers)]
+    wa = W.ATTN_WORKLOADS["attn"]
+    x = W.attn_inputs(wa)
+    d = {k_: torch.from_numpy(np.ascontiguousarray(v_)).to(dev) for k_, v_ in x.items()}
+    apools = (d["k_codes"], d["v_codes"], d["k_scales"], d["v_scales"])
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    levels = []
+    t_start = time.perf_counter()
+    for c in (1, 4, 16, 64, 256):
+        kv_c = [(k_[:c], v_[:c]) for k_, v_ in kvs]
+        app = {r: S.LayersCall(kv_c, slots[:c], pools, h=wl.h, rot=r) for r in ("k", "none")}
+        L = x["context_lens"][:c]
+        maxc = int(L.max())
+        att = {r: S.AttentionCall(d["q"][:c], apools, d["block_tables"][:c],
+                                  d["context_lens"][:c], maxc, h=wa.h, rot=r)
+               for r in ("k", "none")}
+        res = {}
+        for name, calls in (("append", app), ("attention", att)):
+            for fn in calls.values():
+                for _ in range(20):
+                    fn()
+            rot, naive = [], []
+            n = max(20, args.steps // 10)
+            for _ in range(7):
+                naive.append(timed(calls["none"], n))
+                rot.append(timed(calls["k"], n))
+            res[name] = {"rot_us": round(float(np.median(rot)) * 1e3, 3),
+                         "naive_us": round(float(np.median(naive)) * 1e3, 3),
+                         "rot_over_naive": round(float(np.median(rot) / np.median(naive)), 4)}
+        step_rot = res["append"]["rot_us"] + layers * res["attention"]["rot_us"]
+        step_naive = res["append"]["naive_us"] + layers * res["attention"]["naive_us"]
+        levels.append({"concurrency": c, "context_tokens": int(L.sum()),
+                       "append_36_layers": res["append"], "attention_one_layer": res["attention"],
+                       "step_estimate_us": {"rot": round(step_rot, 2), "naive": round(step_naive, 2),
+                                            "rot_over_naive": round(step_rot / step_naive, 4)},
+                       "tokens_per_s": round(c / (step_rot * 1e-6), 1)})
+        print(f"[bench] concurrency {c}: step {step_rot:.1f} us (naive {step_naive:.1f})",
+              file=sys.stderr, flush=True)
+    wall = time.perf_counter() - t_start
+    top = levels[-1]
+    out = {
+        "metric": "decode tokens/s of the INT4 KV path (36-layer append + attention) across "
+                  "concurrency; rotated vs naive INT4",
+        "value": top["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": 20,
+        "ms_per_step": round(top["step_estimate_us"]["rot"] * 1e-3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": ("concurrency sweep: decode recipe (8 KV heads x 128, 36 layers, "
+                                "K-only rotation h=128) for the appends, attn recipe (32 query "
+                                "heads, contexts uniform in [1, 8000], page 16) for attention; "
+                                "step estimate = 36-layer append + 36 x one layer's attention"),
+                   "levels": [l["concurrency"] for l in levels], "parallelism": "single GPU"},
+        "levels": levels,
+        "seconds": round(wall, 1),
+        "roofline": None,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="prefill",
-                    choices=["prefill", "decode", "sweep", "long", "attn"])
+                    choices=["prefill", "decode", "sweep", "long", "attn", "concurrency"])
     ap.add_argument("--h", type=int, default=None)
     ap.add_argument("--rot", default=None, choices=["none", "k", "kv"])
     ap.add_argument("--cpu-sample", type=int, default=131072)
@@ -347,6 +447,9 @@ def main():
 
     if args.workload == "attn":
         bench_attention(args)
+        return
+    if args.workload == "concurrency":
+        bench_concurrency(args)
         return
 
     import torch
