@@ -4,6 +4,7 @@
     python bench.py --workload attn     (decode attention over the INT4 pool)
     python bench.py --workload concurrency  (rotated vs naive INT4 across 1..256
                                              concurrent decodes)
+    python bench.py --heads 1   (one GPU's share of the 8 KV heads under TP-8)
 
 One step = one sawkv_quantize_append call over the workload's batch (rotate,
 token-wise INT4, pack, scatter into the paged pool: the whole write path).
@@ -11,6 +12,8 @@ Inputs are generated, uploaded and resident in HBM before timing starts.
 Prints ONE JSON line. Alongside the step it times, on the same batch:
   * the naive-INT4 control (sawkv_naive_int4_append), interleaved with the
     rotated kernel, for the rotate-vs-naive ratio;
+  * the same two kernels with cold caches (an untimed 1 GiB read before every
+    timed launch);
   * the read-back (sawkv_dequant_gather) of the same slots;
   * (prefill, sweep) the uncompressed fp16 cache write and token-wise INT8
     append / read-back, with INT8's reconstruction error;
@@ -25,6 +28,7 @@ V codes and scales of every context token, the queries, the outputs and the
 block tables.
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -433,6 +437,8 @@ def main():
     ap.add_argument("--workload", default="prefill",
                     choices=["prefill", "decode", "sweep", "long", "attn", "concurrency"])
     ap.add_argument("--h", type=int, default=None)
+    ap.add_argument("--heads", type=int, default=None,
+                    help="KV heads per GPU (e.g. 1 or 2: the TP-8 / TP-4 share of 8 heads)")
     ap.add_argument("--rot", default=None, choices=["none", "k", "kv"])
     ap.add_argument("--cpu-sample", type=int, default=131072)
     ap.add_argument("--no-cpu", action="store_true")
@@ -456,6 +462,9 @@ def main():
     from int4_kv_cache_amd import sawkv as S
 
     wl = W.WORKLOADS[args.workload]
+    if args.heads:
+        # one GPU's share under tensor parallelism over KV heads (8 heads / TP-n)
+        wl = dataclasses.replace(wl, H=args.heads)
     h = args.h or wl.h
     rot = {"none": 0, "k": 1, "kv": 2}[args.rot] if args.rot else wl.rot_mode
     dev = torch.device("cuda:0")
@@ -538,6 +547,34 @@ def main():
         boots.append(np.median(a) / np.median(b))
     ratio_ci = [round(float(np.percentile(boots, 2.5)), 4), round(float(np.percentile(boots, 97.5)), 4)]
 
+    # cold caches: every timed launch follows an untimed read of 1 GiB (larger
+    # than the 256 MB last-level cache plus L2), which leaves only clean lines
+    # behind (a fill would leave dirty ones, whose write-back lands in the timed
+    # launch); rotated and naive interleaved
+    flush = torch.ones(256 * 1024 * 1024, dtype=torch.int32, device=dev)
+    fsum = torch.empty((1,), dtype=torch.int64, device=dev)
+    n_cold = 30 if wl.T * layers <= 262144 else 10
+    cold = {"rot": [], "naive": []}
+    for _ in range(n_cold):
+        for name, fn in (("naive", step_naive), ("rot", step_rot)):
+            torch.sum(flush, dim=(0,), dtype=torch.int64, out=fsum[0])
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            fn()
+            c1.record(stream)
+            torch.cuda.synchronize()
+            cold[name].append(c0.elapsed_time(c1))
+    del flush, fsum
+
+    def pct(a):
+        return {q: round(float(np.percentile(a, v)) * 1e3, 2)
+                for q, v in (("p5", 5), ("median", 50), ("p95", 95))}
+    cold_out = {"rot_us": pct(cold["rot"]), "naive_us": pct(cold["naive"]),
+                "rot_over_naive": round(float(np.median(cold["rot"]) / np.median(cold["naive"])), 4),
+                "GBps_rot_median": round(bytes_step / (np.median(cold["rot"]) * 1e-3) / 1e9, 1),
+                "launches": n_cold,
+                "flush": "1 GiB device read before every timed launch (not timed)"}
+
     # read-back of the same slots
     outs = [(torch.empty_like(kvs[l][0]), torch.empty_like(kvs[l][1])) for l in range(layers)]
     for _ in range(3):
@@ -563,7 +600,8 @@ def main():
     copy_gbps = 2 * cbuf.numel() * 4 / (c_ms * 1e-3) / 1e9
     del cbuf, cdst
 
-    traffic = measured_traffic(args.workload)
+    # the committed counters cover the workloads at their own shapes only
+    traffic = measured_traffic(args.workload) if not args.heads else None
     out = {
         "metric": METRIC,
         "value": round(gbps, 2),
@@ -603,6 +641,7 @@ def main():
         "gather": {"ms_per_step": round(g_ms, 5),
                    "GBps": round(bytes_step / (g_ms * 1e-3) / 1e9, 2),
                    "tokens_per_s": round(tokens / (g_ms * 1e-3), 1)},
+        "cold": cold_out,
         "attainable": {"copy_256MiB_GBps": round(copy_gbps, 1),
                        "note": "torch device-to-device copy on the same GPU, context only"},
         "kernel_source_hash": kernel_source_hash(),
