@@ -960,12 +960,26 @@ __device__ __forceinline__ float quads_max(float v) {
                      __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0x12C, 0xF, 0xF, false))));
 }
 
-// One row of 16 lanes per output vector (4 vectors per wave): quad qd of the
-// row merges chunks qd, qd + 4, ...; the four quads are then merged.
-template <int HB>
+// Sum / max over the four rows of 16 lanes (every lane gets the result).
+__device__ __forceinline__ float rows_sum4(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+__device__ __forceinline__ float rows_max4(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+
+// QPV quads of 4 lanes per output vector: QPV = 4, one row of 16 lanes per
+// vector (4 vectors per wave), or QPV = 16, the whole wave on one vector (for
+// few vectors with many chunks). Quad qd merges chunks qd, qd + QPV, ...;
+// the quads are then merged.
+template <int HB, int QPV>
 __global__ __launch_bounds__(64) void attn_combine_kernel(CombineParams p) {
-  const int lane = threadIdx.x, lam = lane & 3, qd = (lane >> 2) & 3;
-  const int64_t v = (int64_t)blockIdx.x * 4 + (lane >> 4);
+  static_assert(QPV == 4 || QPV == 16, "quads per vector");
+  const int lane = threadIdx.x, lam = lane & 3;
+  const int qd = QPV == 4 ? (lane >> 2) & 3 : lane >> 2;
+  const int64_t v = QPV == 4 ? (int64_t)blockIdx.x * 4 + (lane >> 4) : (int64_t)blockIdx.x;
   const bool live = v < p.n_vec;
   const int64_t b = live ? v / p.Hq : 0;
   const int qh = live ? (int)(v % p.Hq) : 0;
@@ -980,13 +994,13 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(CombineParams p) {
 #pragma unroll
   for (int k = 0; k < kElems; ++k) x[k] = 0.0f;
   float lsum = 0.0f;
-  const int mine = nck > qd ? (nck - qd + 3) / 4 : 0;   // chunks qd + 4k of this quad
+  const int mine = nck > qd ? (nck - qd + QPV - 1) / QPV : 0;   // chunks qd + QPV k
   if (mine > 0) {
     constexpr int kDepth = 4;
     f4_t buf[kDepth][8];
     float2 mlb[kDepth];
     auto fetch = [&](int k, int slot) {
-      const int64_t row = base + (int64_t)(qd + 4 * k) * p.Hq;
+      const int64_t row = base + (int64_t)(qd + QPV * k) * p.Hq;
       mlb[slot] = *reinterpret_cast<const float2*>(p.part_ml + row * 2);
       const f4_t* src = reinterpret_cast<const f4_t*>(p.part_o + row * kD + 8 * lam);
 #pragma unroll
@@ -1028,12 +1042,18 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(CombineParams p) {
       }
     }
   }
-  // merge the four quads of the row
-  const float Mv = quads_max(M);
+  // merge the quads of the vector
+  float Mv = quads_max(M);
+  if constexpr (QPV == 16) Mv = rows_max4(Mv);
   const float rq = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - Mv);
   lsum = quads_sum(lsum * rq);
 #pragma unroll
   for (int k = 0; k < kElems; ++k) x[k] = quads_sum(x[k] * rq);
+  if constexpr (QPV == 16) {
+    lsum = rows_sum4(lsum);
+#pragma unroll
+    for (int k = 0; k < kElems; ++k) x[k] = rows_sum4(x[k]);
+  }
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
 #pragma unroll
   for (int k = 0; k < kElems; ++k) x[k] *= inv;
@@ -1133,9 +1153,13 @@ int g_index(int32_t G) { return G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3; }
 
 const void* const kChunk[4] = {(void*)&attn_chunk_kernel<1>, (void*)&attn_chunk_kernel<2>,
                                (void*)&attn_chunk_kernel<4>, (void*)&attn_chunk_kernel<8>};
-const void* const kCombine[5] = {(void*)&attn_combine_kernel<0>, (void*)&attn_combine_kernel<16>,
-                                 (void*)&attn_combine_kernel<32>, (void*)&attn_combine_kernel<64>,
-                                 (void*)&attn_combine_kernel<128>};
+const void* const kCombine[2][5] = {
+    {(void*)&attn_combine_kernel<0, 4>, (void*)&attn_combine_kernel<16, 4>,
+     (void*)&attn_combine_kernel<32, 4>, (void*)&attn_combine_kernel<64, 4>,
+     (void*)&attn_combine_kernel<128, 4>},
+    {(void*)&attn_combine_kernel<0, 16>, (void*)&attn_combine_kernel<16, 16>,
+     (void*)&attn_combine_kernel<32, 16>, (void*)&attn_combine_kernel<64, 16>,
+     (void*)&attn_combine_kernel<128, 16>}};
 
 int launch64(const void* fn, int64_t blocks, void* params, hipStream_t stream) {
   void* args[] = {params};
@@ -1233,7 +1257,12 @@ int attention_impl(const void* q, int64_t q_stride, const void* k_codes, const v
   mp.C = lay.C;
   mp.max_context = (int32_t)max_context;
   const int hv = rot_mode == SAWKV_ROT_KV ? (h == 16 ? 1 : h == 32 ? 2 : h == 64 ? 3 : 4) : 0;
-  if ((st = launch64(kCombine[hv], (B * Hq + 3) / 4, &mp, s))) return st;
+  // more chunks than one round of 4-deep loads per quad, over few vectors: a
+  // whole wave per vector (16 quads), so each quad merges a quarter as many
+  // chunks; otherwise 4 vectors per wave
+  const bool wide = lay.NC > 16 && B * Hq < 4096;
+  if ((st = launch64(kCombine[wide ? 1 : 0][hv], wide ? B * Hq : (B * Hq + 3) / 4, &mp, s)))
+    return st;
   return ok();
 }
 

@@ -144,6 +144,21 @@ def test_small_all_rotations(env, rot, h):
     assert np.array_equal(got[0], np.zeros_like(got[0]))          # empty context
 
 
+@pytest.mark.parametrize("rot,h", [(O.ROT_NONE, 128), (O.ROT_K, 128), (O.ROT_KV, 128),
+                                   (O.ROT_KV, 32)])
+def test_few_sequences_long_contexts(env, rot, h):
+    """Few sequences, long contexts: more than 16 chunks of 128 tokens over 128
+    output vectors, the case where the merge of the chunks runs one wave per
+    output vector; one empty context among them."""
+    wl = small(B=4, ctx=("list", (6000, 0, 2500, 4100)), wid=40, masked=2, h=h, rot_mode=rot)
+    x = W.attn_inputs(wl)
+    say(f"attn few long contexts rot={ROTS[rot]} h={h} L={x['context_lens'].tolist()}")
+    got = run_gpu(env, x, 6000, h, rot)
+    ref = run_oracle(x, h, rot)
+    check(got, ref, tolerance(x, h, rot, np.arange(wl.B), ref), f"long ctx rot={rot} h={h}")
+    assert np.array_equal(got[1], np.zeros_like(got[1]))
+
+
 @pytest.mark.parametrize("Hq,H", [(8, 8), (16, 8), (64, 8), (4, 1), (2, 2)])
 def test_group_sizes(env, Hq, H):
     wl = small(Hq=Hq, H=H, wid=8 + Hq + H)
