@@ -1109,6 +1109,9 @@ Layout make_layout(int64_t B, int32_t Hq, int32_t H, int64_t max_context) {
   Layout L{};
   int C = 512;
   while (C > 128 && B * H * ((max_context + C - 1) / C) < 8192) C >>= 1;
+  // a grid that cannot fill the chip even at 128 tokens (one or two long
+  // sequences): halve once more, fewer serial steps per wave
+  if (C == 128 && B * H * ((max_context + 127) / 128) < 1024) C = 64;
   L.C = C;
   L.NC = max_context > 0 ? (max_context + C - 1) / C : 1;
   size_t off = 0;
