@@ -531,7 +531,11 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
   // chunk-major: every sequence's first chunk, then every second chunk, ...,
   // so the last blocks dispatched are the final chunks of the longest contexts
   const uint32_t nb = p.n_groups / (uint32_t)p.NC;
-  const int c = (int)(grp / nb), b = (int)(grp % nb);
+  // the groups of XCD x are those with grp % 8 == x; offsetting the sequence
+  // by the chunk index sends chunk c of sequence b to XCD (b + c) % 8 (when
+  // nb % 8 == 0), so every XCD gets a share of every context, not whole ones
+  const int c = (int)(grp / nb);
+  const int b = (int)((grp % nb + nb - (uint32_t)c % nb) % nb);
   const uint32_t part = (uint32_t)b * p.NC + c;    // partial slot (b, c)
   int L = p.context_lens[b];
   L = L < 0 ? 0 : (L > p.max_context ? p.max_context : L);
@@ -824,7 +828,11 @@ __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
   // chunk-major: every sequence's first chunk, then every second chunk, ...,
   // so the last blocks dispatched are the final chunks of the longest contexts
   const uint32_t nb = p.n_groups / (uint32_t)p.NC;
-  const int c = (int)(grp / nb), b = (int)(grp % nb);
+  // the groups of XCD x are those with grp % 8 == x; offsetting the sequence
+  // by the chunk index sends chunk c of sequence b to XCD (b + c) % 8 (when
+  // nb % 8 == 0), so every XCD gets a share of every context, not whole ones
+  const int c = (int)(grp / nb);
+  const int b = (int)((grp % nb + nb - (uint32_t)c % nb) % nb);
   const uint32_t part = (uint32_t)b * p.NC + c;    // partial slot (b, c)
   int L = p.context_lens[b];
   L = L < 0 ? 0 : (L > p.max_context ? p.max_context : L);
