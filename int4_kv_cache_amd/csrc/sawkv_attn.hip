@@ -528,17 +528,22 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
   const int h = (int)(r8 % (uint32_t)p.H);
   const uint32_t grp = (r8 / (uint32_t)p.H) * 8u + (bx & 7u);
   if (grp >= p.n_groups) return;
-  // chunk-major: every sequence's first chunk, then every second chunk, ...,
-  // so the last blocks dispatched are the final chunks of the longest contexts
+  // Groups of chunks in dispatch order, counted from the end of each context:
+  // group r holds chunk nck - NC + r of every sequence (nck = its chunk
+  // count), so whole chunks go first and the partial last chunks (r = NC - 1)
+  // last, which keeps the final round of waves short (longest work first).
   const uint32_t nb = p.n_groups / (uint32_t)p.NC;
   // the groups of XCD x are those with grp % 8 == x; offsetting the sequence
-  // by the chunk index sends chunk c of sequence b to XCD (b + c) % 8 (when
-  // nb % 8 == 0), so every XCD gets a share of every context, not whole ones
-  const int c = (int)(grp / nb);
-  const int b = (int)((grp % nb + nb - (uint32_t)c % nb) % nb);
-  const uint32_t part = (uint32_t)b * p.NC + c;    // partial slot (b, c)
+  // by r spreads the chunks of one sequence over the XCDs (when nb % 8 == 0
+  // group r of sequence b goes to XCD (b + r) % 8), so every XCD gets a share
+  // of every context, not whole ones
+  const int r = (int)(grp / nb);
+  const int b = (int)((grp % nb + nb - (uint32_t)r % nb) % nb);
   int L = p.context_lens[b];
   L = L < 0 ? 0 : (L > p.max_context ? p.max_context : L);
+  const int c = (L + p.C - 1) / p.C - p.NC + r;     // chunk index; < 0: none
+  if (c < 0) return;
+  const uint32_t part = (uint32_t)b * p.NC + c;    // partial slot (b, c)
   const int t_begin = c * p.C;
   if (t_begin >= L) return;
   const int t_end = min(t_begin + p.C, L);
@@ -825,17 +830,22 @@ __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
   const int hp = (int)(r8 % (uint32_t)HP);
   const uint32_t grp = (r8 / (uint32_t)HP) * 8u + (bx & 7u);
   if (grp >= p.n_groups) return;
-  // chunk-major: every sequence's first chunk, then every second chunk, ...,
-  // so the last blocks dispatched are the final chunks of the longest contexts
+  // Groups of chunks in dispatch order, counted from the end of each context:
+  // group r holds chunk nck - NC + r of every sequence (nck = its chunk
+  // count), so whole chunks go first and the partial last chunks (r = NC - 1)
+  // last, which keeps the final round of waves short (longest work first).
   const uint32_t nb = p.n_groups / (uint32_t)p.NC;
   // the groups of XCD x are those with grp % 8 == x; offsetting the sequence
-  // by the chunk index sends chunk c of sequence b to XCD (b + c) % 8 (when
-  // nb % 8 == 0), so every XCD gets a share of every context, not whole ones
-  const int c = (int)(grp / nb);
-  const int b = (int)((grp % nb + nb - (uint32_t)c % nb) % nb);
-  const uint32_t part = (uint32_t)b * p.NC + c;    // partial slot (b, c)
+  // by r spreads the chunks of one sequence over the XCDs (when nb % 8 == 0
+  // group r of sequence b goes to XCD (b + r) % 8), so every XCD gets a share
+  // of every context, not whole ones
+  const int r = (int)(grp / nb);
+  const int b = (int)((grp % nb + nb - (uint32_t)r % nb) % nb);
   int L = p.context_lens[b];
   L = L < 0 ? 0 : (L > p.max_context ? p.max_context : L);
+  const int c = (L + p.C - 1) / p.C - p.NC + r;     // chunk index; < 0: none
+  if (c < 0) return;
+  const uint32_t part = (uint32_t)b * p.NC + c;    // partial slot (b, c)
   const int t_begin = c * p.C;
   if (t_begin >= L) return;
   const int t_end = min(t_begin + p.C, L);
