@@ -284,6 +284,29 @@ def bench_attention(args):
         rot_ms.append(timed(call, n_ab))
     ratio = float(np.median(rot_ms) / np.median(naive_ms))
 
+    # other query-head groupings on the same pool (fresh queries): 8 per KV
+    # head (64 query heads, as Llama-2-70B) and 1 (multi-head attention)
+    groupings = []
+    for hq in (8 * wl.H, wl.H):
+        qg = torch.from_numpy(W.attn_queries(wl, hq)).to(dev)
+        cg = S.AttentionCall(qg, pools, d["block_tables"], d["context_lens"], maxc, h=h,
+                             rot=ROT_NAME[rot])
+        ng = S.AttentionCall(qg, pools, d["block_tables"], d["context_lens"], maxc, h=h,
+                             rot="none", workspace=cg.workspace)
+        for _ in range(10):
+            cg()
+            ng()
+        gr, gn = [], []
+        for _ in range(5):
+            gn.append(timed(ng, 50))
+            gr.append(timed(cg, 50))
+        gb = attn_bytes(dataclasses.replace(wl, Hq=hq), x)
+        groupings.append({"query_heads": hq, "kv_heads": wl.H,
+                          "us": round(float(np.median(gr)) * 1e3, 2),
+                          "GBps": round(gb / (np.median(gr) * 1e-3) / 1e9, 1),
+                          "rot_over_naive": round(float(np.median(gr) / np.median(gn)), 4)})
+        del cg, ng, qg
+
     traffic = measured_traffic("attn", ATTN_SRC)
     out = {
         "metric": ATTN_METRIC,
@@ -320,6 +343,7 @@ def bench_attention(args):
                      "naive_ms_median": round(float(np.median(naive_ms)), 5),
                      "rot_over_naive": round(ratio, 4), "rounds": rounds,
                      "steps_per_round": n_ab},
+        "other_head_groupings": groupings,
         "workspace_bytes": int(call.workspace.numel()),
         "kernel_source_hash": kernel_source_hash(ATTN_SRC),
     }

@@ -441,16 +441,20 @@ __device__ __forceinline__ void compute_step(const StepRegs& r, const uint32_t (
     const float alpha = need ? __builtin_amdgcn_exp2f((a.m - mn) * 0.25f) : 1.0f;
     a.l *= alpha;
     a.W *= alpha;
-    float al[G];
-#pragma unroll
-    for (int qc = 0; qc < G; ++qc)
-      al[qc] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                             __builtin_bit_cast(int, alpha), qc));
+    // factor of query j (G < 8) or of query j / 4 + j (G = 8, by lane group);
+    // both candidates are read as uniform values and selected per lane, so no
+    // array is indexed with a lane-dependent value (that would go to scratch)
+    const int ab = __builtin_bit_cast(int, alpha);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float f;
-      if constexpr (G == 8) f = (g & 1) ? al[4 + j] : al[j];
-      else f = al[j % G];
+      if constexpr (G == 8) {
+        const float f0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ab, j));
+        const float f1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ab, 4 + j));
+        f = (g & 1) ? f1 : f0;
+      } else {
+        f = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ab, j % G));
+      }
 #pragma unroll
       for (int k = 0; k < 8; ++k) a.o[k][j] *= f;
     }
@@ -619,10 +623,7 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) os[k][j] = j < G ? a.o[k][j] + a.o[k][j + G] : 0.0f;
   }
-  float Wq[G];
-#pragma unroll
-  for (int qc = 0; qc < G; ++qc)
-    Wq[qc] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, W), qc));
+  const int Wb = __builtin_bit_cast(int, W);
 
   const int64_t head0 = (int64_t)part * p.Hq + (int64_t)h * G;
   const bool writer = G == 8 ? g < 2 : g == 0;
@@ -631,8 +632,13 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
     for (int j = 0; j < (G < 4 ? G : 4); ++j) {
       const int qi = G == 8 ? 4 * g + j : j;
       float Wv;
-      if constexpr (G == 8) Wv = g ? Wq[4 + (j & 3)] : Wq[j & 3];
-      else Wv = Wq[j % G];
+      if constexpr (G == 8) {
+        const float w0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(Wb, j & 3));
+        const float w1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(Wb, 4 + (j & 3)));
+        Wv = g ? w1 : w0;
+      } else {
+        Wv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(Wb, j % G));
+      }
       float vals[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k)

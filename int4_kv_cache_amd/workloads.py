@@ -52,7 +52,9 @@ under test. Recipe, key (seed, workload id, 3, part[, chunk]):
             -8 included, occurs), sampled through a 65536-entry byte table
   scales    part 4 (K) / 5 (V): fp16 of base[head] * lognormal(0, 0.3), base
             0.35, and 20x that on two heads per tensor (outlier heads)
-  queries   part 6: fp16 standard normal [B, Hq, D]
+  queries   part 6: fp16 standard normal [B, Hq, D]; queries for another
+            number of query heads Hq' over the same pool: key
+            (seed, workload id, 3, 6, Hq')
 """
 
 import os
@@ -331,7 +333,15 @@ def attn_inputs(wl):
         ln = r.lognormal(0.0, 0.3, size=(N_pg, wl.P, wl.H))
         scales.append((ln * base[None, None, :]).astype(np.float16))
 
-    r = np.random.default_rng([wl.seed, wl.wid, 3, 6])
-    q = r.standard_normal((wl.B, wl.Hq, wl.D), dtype=np.float32).astype(np.float16)
-    return {"q": q, "k_codes": codes[0], "v_codes": codes[1], "k_scales": scales[0],
-            "v_scales": scales[1], "block_tables": bt, "context_lens": L}
+    return {"q": attn_queries(wl), "k_codes": codes[0], "v_codes": codes[1],
+            "k_scales": scales[0], "v_scales": scales[1], "block_tables": bt,
+            "context_lens": L}
+
+
+def attn_queries(wl, Hq=None):
+    """The queries of an attention workload alone, fp16 [B, Hq, D] (part 6 of
+    the recipe); with another Hq they are a fresh draw for the same pool (the
+    pool does not depend on the number of query heads)."""
+    Hq = wl.Hq if Hq is None else Hq
+    r = np.random.default_rng([wl.seed, wl.wid, 3, 6] + ([] if Hq == wl.Hq else [Hq]))
+    return r.standard_normal((wl.B, Hq, wl.D), dtype=np.float32).astype(np.float16)
