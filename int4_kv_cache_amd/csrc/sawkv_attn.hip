@@ -1126,9 +1126,11 @@ struct Layout {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Chunk length: 512 tokens, halved (down to 64) while the step would have
+// Chunk length: 512 tokens, halved (down to 128) while the step would have
 // fewer than 8192 (sequence, chunk, head) items, so that small batches still
-// spread over every compute unit.
+// spread over every compute unit; 64 only for grids too small to fill the
+// chip even at 128 (each wave then pays the query preparation for fewer
+// tokens, which costs more than it gains once the grid is large enough).
 Layout make_layout(int64_t B, int32_t Hq, int32_t H, int64_t max_context) {
   Layout L{};
   int C = 512;
