@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
     python bench.py --workload attn     (decode attention over the INT4 pool)
+    python bench.py --workload attn_long  (the same over 64 contexts of 32768 tokens)
     python bench.py --workload concurrency  (rotated vs naive INT4 across 1..256
                                              concurrent decodes)
     python bench.py --heads 1   (one GPU's share of the 8 KV heads under TP-8)
@@ -226,20 +227,20 @@ def attn_cpu_baseline(wl, x, h, rot, budget_s=12.0):
     gbps = toks * wl.bytes_per_token() / dt / 1e9
     return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "decode_tokens_per_s": round(n / dt, 2), "seconds": round(dt, 2),
-            "sample": f"first {n} of {wl.B} sequences ({toks} context tokens) of the attn "
-                      f"batch, numpy float64 oracle, single thread"}
+            "sample": f"first {n} of {wl.B} sequences ({toks} context tokens) of the "
+                      f"{wl.name} batch, numpy float64 oracle, single thread"}
 
 
 def bench_attention(args):
     import torch
     from int4_kv_cache_amd import sawkv as S
 
-    wl = W.ATTN_WORKLOADS["attn"]
+    wl = W.ATTN_WORKLOADS[args.workload]
     h = args.h or wl.h
     rot = {"none": 0, "k": 1, "kv": 2}[args.rot] if args.rot else wl.rot_mode
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    print(f"[bench] generating attn inputs", file=sys.stderr, flush=True)
+    print(f"[bench] generating {wl.name} inputs", file=sys.stderr, flush=True)
     x = W.attn_inputs(wl)
     d = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in x.items()}
     pools = (d["k_codes"], d["v_codes"], d["k_scales"], d["v_scales"])
@@ -307,7 +308,7 @@ def bench_attention(args):
                           "rot_over_naive": round(float(np.median(gr) / np.median(gn)), 4)})
         del cg, ng, qg
 
-    traffic = measured_traffic("attn", ATTN_SRC)
+    traffic = measured_traffic(wl.name, ATTN_SRC)
     out = {
         "metric": ATTN_METRIC,
         "value": round(gbps, 2),
@@ -321,7 +322,7 @@ def bench_attention(args):
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": (f"attn: {wl.B} sequences x 1 query token, contexts uniform "
+        "config": {"workload": (f"{wl.name}: {wl.B} sequences x 1 query token, contexts uniform "
                                 f"in [{wl.ctx[1]}, {wl.ctx[2]}] ({int(L.sum())} tokens, max "
                                 f"{maxc}), {wl.Hq} query / {wl.H} KV heads x {wl.D}, page "
                                 f"{wl.P}, INT4 pool rotation {ROT_NAME[rot]} h={h}"),
@@ -459,7 +460,8 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="prefill",
-                    choices=["prefill", "decode", "sweep", "long", "attn", "concurrency"])
+                    choices=["prefill", "decode", "sweep", "long", "attn", "attn_long",
+                             "concurrency"])
     ap.add_argument("--h", type=int, default=None)
     ap.add_argument("--heads", type=int, default=None,
                     help="KV heads per GPU (e.g. 1 or 2: the TP-8 / TP-4 share of 8 heads)")
@@ -475,7 +477,7 @@ def main():
               file=sys.stderr, flush=True)
         sys.exit(2)
 
-    if args.workload == "attn":
+    if args.workload in ("attn", "attn_long"):
         bench_attention(args)
         return
     if args.workload == "concurrency":

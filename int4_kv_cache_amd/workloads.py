@@ -250,6 +250,10 @@ ATTN_WORKLOADS = {
     # 128, page 16, K-only rotation) with 32 query heads (4 per KV head) and
     # contexts of 1 to 8000 tokens.
     "attn": AttnWorkload("attn", 6, 256, 32, 8, 128, 16, ("uniform", 1, 8000), 128, ROT_K),
+    # Long contexts: the long append workload's shape (64 sequences of 32768
+    # tokens, page 32) read by one decode step, 2.2 GB of K/V per layer.
+    "attn_long": AttnWorkload("attn_long", 9, 64, 32, 8, 128, 32, ("uniform", 32768, 32768),
+                              128, ROT_K),
     # Small cases the oracle finishes in seconds: ragged lengths around the
     # 16-token tiles and 32-token steps, an empty context and masked pages.
     "attn_small": AttnWorkload("attn_small", 7, 9, 32, 8, 128, 16,

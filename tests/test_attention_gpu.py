@@ -278,3 +278,17 @@ def test_full_size_sampled(env):
     ref = run_oracle(x, wl.h, wl.rot_mode, seqs=seqs)
     check(got[seqs], ref, tolerance(x, wl.h, wl.rot_mode, seqs, ref), "full sampled")
     assert np.all(np.isfinite(got))
+
+
+def test_long_contexts_sampled(env):
+    """64 contexts of 32768 tokens (page 32, 64 chunks per sequence): three
+    sequences against the oracle, every output finite."""
+    wl = W.ATTN_WORKLOADS["attn_long"]
+    x = W.attn_inputs(wl)
+    maxc = int(x["context_lens"].max())
+    say(f"attn long contexts B={wl.B} L={maxc} P={wl.P}")
+    got = run_gpu(env, x, maxc, wl.h, wl.rot_mode)
+    seqs = np.array([0, 31, 63])
+    ref = run_oracle(x, wl.h, wl.rot_mode, seqs=seqs)
+    check(got[seqs], ref, tolerance(x, wl.h, wl.rot_mode, seqs, ref), "long sampled")
+    assert np.all(np.isfinite(got))
