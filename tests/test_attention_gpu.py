@@ -159,7 +159,10 @@ def test_few_sequences_long_contexts(env, rot, h):
     assert np.array_equal(got[1], np.zeros_like(got[1]))
 
 
-@pytest.mark.parametrize("Hq,H", [(8, 8), (16, 8), (64, 8), (4, 1), (2, 2)])
+# four queries per KV head and an even H run the head-pair kernel (H = 2, 4, 6,
+# 16 besides the default 8); an odd H (4, 1) the single-head kernel
+@pytest.mark.parametrize("Hq,H", [(8, 8), (16, 8), (64, 8), (4, 1), (2, 2),
+                                  (8, 2), (16, 4), (24, 6), (64, 16)])
 def test_group_sizes(env, Hq, H):
     wl = small(Hq=Hq, H=H, wid=8 + Hq + H)
     x = W.attn_inputs(wl)
