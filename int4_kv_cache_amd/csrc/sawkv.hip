@@ -190,6 +190,7 @@ struct LayersParams {
   int64_t k_stride, v_stride;
   int32_t n_tensors;     // 1 or 2 per layer
   int32_t only_v;        // n_tensors == 1 and that tensor is V
+  int32_t n_layers;
   LayerPtrs layer[kMaxLayers];
 };
 
@@ -197,8 +198,12 @@ static_assert(sizeof(LayersParams) <= 4096, "kernel arguments must stay within 4
 
 template <int HB0, int HB1>
 __global__ __launch_bounds__(kThreads) void append_layers_kernel(LayersParams p) {
-  const int slot_in_layer = (int)(blockIdx.y % (unsigned)p.n_tensors);
-  const LayerPtrs& L = p.layer[blockIdx.y / (unsigned)p.n_tensors];
+  // tensor-major: every layer's first tensor (K, the rotated one under
+  // K-only rotation) is dispatched before any second tensor, so in a launch
+  // of one round of waves the data that arrives last feeds the shorter
+  // (unrotated) arithmetic
+  const int slot_in_layer = (int)(blockIdx.y / (unsigned)p.n_layers);
+  const LayerPtrs& L = p.layer[blockIdx.y % (unsigned)p.n_layers];
   const bool is_v = p.n_tensors == 2 ? slot_in_layer == 1 : p.only_v != 0;
   const AppendTensor A = is_v ? AppendTensor{L.v, p.v_stride, L.v_codes, L.v_scales}
                               : AppendTensor{L.k, p.k_stride, L.k_codes, L.k_scales};
@@ -593,6 +598,7 @@ int append_layers_impl(const sawkv_layer_t* layers, int32_t n_layers, int64_t k_
   if (has_k) hb[n++] = hb_index(h, rot_mode != SAWKV_ROT_NONE);
   if (has_v) hb[n++] = hb_index(h, rot_mode == SAWKV_ROT_KV);
   p.n_tensors = n;
+  p.n_layers = n_layers;
   p.only_v = (!has_k && has_v) ? 1 : 0;
   p.k_stride = k_stride;
   p.v_stride = v_stride;
