@@ -169,10 +169,57 @@ __device__ __forceinline__ bool column_hi(int n) {
 // the lower lane takes fma(a, 1, b) = f32(a + b), the upper fma(b, -1, a) =
 // f32(a - b), the same butterflies in the same order as the definition. The
 // query's reductions run over its own LQ lanes.
+// The fp16 query channels of the calling lane, as loaded (CPL / 2 words).
 template <int G, bool PAIR>
-__device__ __forceinline__ void prepare_query(const QueryParams& p, int64_t b, int hg, int lane,
-                                              float (*xs)[kD], u4_t (&bq)[4], float& cinit_n,
-                                              float& F_n) {
+struct QueryRaw {
+  static constexpr int NQ = PAIR ? 2 * G : G;
+  static constexpr int CPL = kD / (64 / NQ);
+  uint32_t w[CPL / 2];
+};
+
+// Issues the load of the calling lane's query channels (see prepare_query for
+// the lane layout); rows are 16-byte aligned (q and q_stride).
+template <int G, bool PAIR>
+__device__ __forceinline__ QueryRaw<G, PAIR> load_query(const QueryParams& p, int64_t b, int hg,
+                                                        int lane) {
+  using R = QueryRaw<G, PAIR>;
+  constexpr int LQ = 64 / R::NQ;
+  const int g = lane / LQ, j = lane % LQ;
+  const __half* row = p.q + b * p.q_stride + (int64_t)(hg * R::NQ + g) * kD + j * R::CPL;
+  R raw;
+  if constexpr (R::CPL >= 8) {
+#pragma unroll
+    for (int c = 0; c < R::CPL / 8; ++c) {
+      const uint4 w = reinterpret_cast<const uint4*>(row)[c];
+      raw.w[4 * c] = w.x;
+      raw.w[4 * c + 1] = w.y;
+      raw.w[4 * c + 2] = w.z;
+      raw.w[4 * c + 3] = w.w;
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < R::CPL / 2; ++m) raw.w[m] = reinterpret_cast<const uint32_t*>(row)[m];
+  }
+  return raw;
+}
+
+// The B operand of the score MFMAs for the calling lane (bq), and for the
+// lane's column n = lane % 16 the accumulator start value (minus 8 times the
+// sum of the query's effective multipliers, cinit) and the log2-unit scale F.
+// The wave's queries are those of head group `hg` of sequence b: one KV head,
+// or a pair of KV heads (PAIR); `raw` is what load_query returned for them.
+// xs: NQ x 128 floats of LDS. One wave.
+//
+// Query g of the wave is held by LQ = 64 / NQ consecutive lanes, CPL = 2 NQ
+// contiguous channels per lane, so the Walsh-Hadamard stages of stride < CPL
+// are in-lane and the others pair lane j of the query with lane j ^ (s / CPL):
+// the lower lane takes fma(a, 1, b) = f32(a + b), the upper fma(b, -1, a) =
+// f32(a - b), the same butterflies in the same order as the definition. The
+// query's reductions run over its own LQ lanes.
+template <int G, bool PAIR>
+__device__ __forceinline__ void prepare_query(const QueryParams& p, const QueryRaw<G, PAIR>& raw,
+                                              int lane, float (*xs)[kD], u4_t (&bq)[4],
+                                              float& cinit_n, float& F_n) {
   constexpr int NQ = PAIR ? 2 * G : G;          // queries of the wave
   static_assert(!PAIR || G == 4, "head pairs are laid out for 4 queries per head");
   constexpr int LQ = 64 / NQ;                   // lanes per query
@@ -180,29 +227,11 @@ __device__ __forceinline__ void prepare_query(const QueryParams& p, int64_t b, i
   const int g = lane / LQ, j = lane % LQ;
 
   float x[CPL];
-  {
-    // rows are 16-byte aligned (q and q_stride); CPL halves from channel j * CPL
-    const __half* row = p.q + b * p.q_stride + (int64_t)(hg * NQ + g) * kD + j * CPL;
-    if constexpr (CPL >= 8) {
 #pragma unroll
-      for (int c = 0; c < CPL / 8; ++c) {
-        const uint4 w = reinterpret_cast<const uint4*>(row)[c];
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const __half2 hv = __builtin_bit_cast(__half2, ws[m]);
-          x[8 * c + 2 * m] = __low2float(hv);
-          x[8 * c + 2 * m + 1] = __high2float(hv);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < CPL / 2; ++m) {
-        const __half2 hv = reinterpret_cast<const __half2*>(row)[m];
-        x[2 * m] = __low2float(hv);
-        x[2 * m + 1] = __high2float(hv);
-      }
-    }
+  for (int m = 0; m < CPL / 2; ++m) {
+    const __half2 hv = __builtin_bit_cast(__half2, raw.w[m]);
+    x[2 * m] = __low2float(hv);
+    x[2 * m + 1] = __high2float(hv);
   }
   if (p.rot_k) {
 #pragma unroll
@@ -351,6 +380,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 
 // Issues the loads of the step at t0 into r. `pages` holds the page id of
 // block (blk0 + lane) of the sequence in lane `lane`.
+template <bool BRANCHLESS>
 __device__ __forceinline__ void load_step(const ChunkParams& p, StepRegs& r, int t0, int t_end,
                                           int blk0, int pages, int h, const Lanes& ln) {
   const uint32_t row_bytes = (uint32_t)p.H * (kD / 2);
@@ -362,12 +392,14 @@ __device__ __forceinline__ void load_step(const ChunkParams& p, StepRegs& r, int
     int page = -1;
     if (st < t_end) page = __builtin_amdgcn_readlane(pages, st / p.P - blk0);
     r.ok[T] = page >= 0 && page < p.N_pg;
-    row[T] = 0;
-    if (r.ok[T]) {
-      const int64_t row0 = ((int64_t)page * p.P + st % p.P) * p.H + h;
-      row[T] = row0;
-      const __amdgpu_buffer_rsrc_t rk = rsrc(p.k_codes + row0 * (kD / 2), tile_bytes);
-      const __amdgpu_buffer_rsrc_t rv = rsrc(p.v_codes + row0 * (kD / 2), tile_bytes);
+    const int64_t row0 = r.ok[T] ? ((int64_t)page * p.P + st % p.P) * p.H + h : 0;
+    row[T] = row0;
+    if (BRANCHLESS || r.ok[T]) {
+      // (branchless: an invalid tile gets an empty buffer range, whose loads
+      // touch no memory and return zeros)
+      const uint32_t reach = r.ok[T] ? tile_bytes : 0u;
+      const __amdgpu_buffer_rsrc_t rk = rsrc(p.k_codes + row0 * (kD / 2), reach);
+      const __amdgpu_buffer_rsrc_t rv = rsrc(p.v_codes + row0 * (kD / 2), reach);
       r.kq[T] = __builtin_amdgcn_raw_buffer_load_b128(rk, ln.k_off, 0, 0);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -515,7 +547,7 @@ __device__ __forceinline__ void compute_step(const StepRegs& r, const uint32_t (
   }
 }
 
-template <int G>
+template <int G, bool EARLY>
 __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
   __shared__ uint16_t sstage[64];
@@ -556,11 +588,9 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
   const int blk0 = t_begin / p.P;
   const int n_blk = (t_end - 1) / p.P - blk0 + 1;
   const int pages = lane < n_blk ? p.block_tables[(int64_t)b * p.bt_stride + blk0 + lane] : -1;
-
-  u4_t bq[4];
-  float cinit, F;
-  prepare_query<G, false>(p.qp, b, h, lane, xs, bq, cinit, F);
-  const float F4 = 4.0f * F;
+  // the query's load goes out between the page ids and the first step, so
+  // each wait takes only what it needs (loads complete in issue order)
+  const QueryRaw<G, false> qraw = load_query<G, false>(p.qp, b, h, lane);
 
   Lanes ln;
   const uint32_t row_bytes = (uint32_t)p.H * (kD / 2);
@@ -579,12 +609,22 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
   for (int k = 0; k < 8; ++k) a.o[k] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   // one step of look-ahead: the loads of step t0 + 32 are in flight while
-  // step t0 is computed
+  // step t0 is computed. EARLY: the first step's loads are issued before the
+  // query is prepared, which then overlaps their latency.
   StepRegs cur, nxt;
-  load_step(p, cur, t_begin, t_end, blk0, pages, h, ln);
+  u4_t bq[4];
+  float cinit, F;
+  if constexpr (EARLY) {
+    load_step<true>(p, cur, t_begin, t_end, blk0, pages, h, ln);
+    prepare_query<G, false>(p.qp, qraw, lane, xs, bq, cinit, F);
+  } else {
+    prepare_query<G, false>(p.qp, qraw, lane, xs, bq, cinit, F);
+    load_step<false>(p, cur, t_begin, t_end, blk0, pages, h, ln);
+  }
+  const float F4 = 4.0f * F;
   for (int t0 = t_begin; t0 < t_end; t0 += kStep) {
     const int t1 = t0 + kStep;
-    if (t1 < t_end) load_step(p, nxt, t1, t_end, blk0, pages, h, ln);
+    if (t1 < t_end) load_step<false>(p, nxt, t1, t_end, blk0, pages, h, ln);
     sstage[lane] = (uint16_t)cur.sc;
     __builtin_amdgcn_wave_barrier();
     uint32_t ks[2][2], vs[2][2];
@@ -678,6 +718,7 @@ struct PairLanes {
   const uint16_t* s_ptr;  // the lane's scale (loader role), relative to the block
 };
 
+template <bool BRANCHLESS>
 __device__ __forceinline__ void load_pair_step(const ChunkParams& p, StepRegs& r, int t0,
                                                int t_end, int blk0, int pages, int h0,
                                                const PairLanes& ln) {
@@ -686,10 +727,11 @@ __device__ __forceinline__ void load_pair_step(const ChunkParams& p, StepRegs& r
   if (t0 < t_end) page = __builtin_amdgcn_readlane(pages, t0 / p.P - blk0);
   const bool ok = page >= 0 && page < p.N_pg;
   r.ok[0] = r.ok[1] = ok;
-  int64_t row0 = 0;
-  if (ok) {
-    row0 = ((int64_t)page * p.P + t0 % p.P) * p.H + h0;
-    const uint32_t reach = 15u * row_bytes + 2u * (kD / 2);   // 16 tokens, two heads
+  const int64_t row0 = ok ? ((int64_t)page * p.P + t0 % p.P) * p.H + h0 : 0;
+  if (BRANCHLESS || ok) {
+    // (branchless: an invalid block gets an empty buffer range, whose loads
+    // touch no memory and return zeros)
+    const uint32_t reach = ok ? 15u * row_bytes + 2u * (kD / 2) : 0u;   // 16 tokens, two heads
     const __amdgpu_buffer_rsrc_t rk = rsrc(p.k_codes + row0 * (kD / 2), reach);
     const __amdgpu_buffer_rsrc_t rv = rsrc(p.v_codes + row0 * (kD / 2), reach);
 #pragma unroll
@@ -821,6 +863,7 @@ __device__ __forceinline__ void compute_pair_step(const StepRegs& r, const uint3
   }
 }
 
+template <bool EARLY>
 __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
   constexpr int G = 4;
   __shared__ uint16_t sstage[64];
@@ -860,11 +903,9 @@ __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
   const int blk0 = t_begin / p.P;
   const int n_blk = (t_end - 1) / p.P - blk0 + 1;
   const int pages = lane < n_blk ? p.block_tables[(int64_t)b * p.bt_stride + blk0 + lane] : -1;
-
-  u4_t bq[4];
-  float cinit, F;
-  prepare_query<G, true>(p.qp, b, hp, lane, xs, bq, cinit, F);
-  const float F4 = 4.0f * F;
+  // the query's load goes out between the page ids and the first step, so
+  // each wait takes only what it needs (loads complete in issue order)
+  const QueryRaw<G, true> qraw = load_query<G, true>(p.qp, b, hp, lane);
   const bool head_ok = (n >> 3) == (g & 1);
 
   PairLanes ln;
@@ -894,11 +935,22 @@ __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) a.o[k] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // EARLY: the first step's loads are issued before the query is prepared,
+  // which then overlaps their latency
   StepRegs cur, nxt;
-  load_pair_step(p, cur, t_begin, t_end, blk0, pages, h0, ln);
+  u4_t bq[4];
+  float cinit, F;
+  if constexpr (EARLY) {
+    load_pair_step<true>(p, cur, t_begin, t_end, blk0, pages, h0, ln);
+    prepare_query<G, true>(p.qp, qraw, lane, xs, bq, cinit, F);
+  } else {
+    prepare_query<G, true>(p.qp, qraw, lane, xs, bq, cinit, F);
+    load_pair_step<false>(p, cur, t_begin, t_end, blk0, pages, h0, ln);
+  }
+  const float F4 = 4.0f * F;
   for (int t0 = t_begin; t0 < t_end; t0 += 16) {
     const int t1 = t0 + 16;
-    if (t1 < t_end) load_pair_step(p, nxt, t1, t_end, blk0, pages, h0, ln);
+    if (t1 < t_end) load_pair_step<false>(p, nxt, t1, t_end, blk0, pages, h0, ln);
     sstage[lane] = (uint16_t)cur.sc;
     __builtin_amdgcn_wave_barrier();
     uint32_t ks[2][2], vs[2][2];
@@ -1180,8 +1232,22 @@ using sawkv::attn::attn_combine_kernel;
 
 int g_index(int32_t G) { return G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3; }
 
-const void* const kChunk[4] = {(void*)&attn_chunk_kernel<1>, (void*)&attn_chunk_kernel<2>,
-                               (void*)&attn_chunk_kernel<4>, (void*)&attn_chunk_kernel<8>};
+// [first-step order][G]: EARLY instantiations issue the first step's loads
+// before preparing the query
+const void* const kChunk[2][4] = {
+    {(void*)&attn_chunk_kernel<1, false>, (void*)&attn_chunk_kernel<2, false>,
+     (void*)&attn_chunk_kernel<4, false>, (void*)&attn_chunk_kernel<8, false>},
+    {(void*)&attn_chunk_kernel<1, true>, (void*)&attn_chunk_kernel<2, true>,
+     (void*)&attn_chunk_kernel<4, true>, (void*)&attn_chunk_kernel<8, true>}};
+const void* const kChunkPair[2] = {(void*)&attn_chunk_pair_kernel<false>,
+                                   (void*)&attn_chunk_pair_kernel<true>};
+
+// A grid of at most four rounds of resident chunk waves (3 per SIMD on 256
+// compute units) issues each wave's first loads before its query
+// preparation: few rounds leave that latency on the critical path. Deeper
+// grids hide it behind other waves, and there the early loads measured
+// slightly slower.
+constexpr int64_t kEarlyIssueBlocks = 4 * 3 * 4 * 256;
 const void* const kCombine[2][5] = {
     {(void*)&attn_combine_kernel<0, 4>, (void*)&attn_combine_kernel<16, 4>,
      (void*)&attn_combine_kernel<32, 4>, (void*)&attn_combine_kernel<64, 4>,
@@ -1270,9 +1336,10 @@ int attention_impl(const void* q, int64_t q_stride, const void* k_codes, const v
   cp.max_context = (int32_t)max_context;
   cp.n_groups = (uint32_t)(B * lay.NC);
   const int64_t chunk_blocks = ((B * lay.NC + 7) / 8) * 8 * groups;
+  const int early = chunk_blocks <= kEarlyIssueBlocks ? 1 : 0;
   if (max_context > 0 &&
-      (st = launch64(pair ? (const void*)&attn_chunk_pair_kernel : kChunk[g_index(G)],
-                     chunk_blocks, &cp, s)))
+      (st = launch64(pair ? kChunkPair[early] : kChunk[early][g_index(G)], chunk_blocks, &cp,
+                     s)))
     return st;
 
   sawkv::attn::CombineParams mp{};

@@ -295,3 +295,26 @@ def test_long_contexts_sampled(env):
     ref = run_oracle(x, wl.h, wl.rot_mode, seqs=seqs)
     check(got[seqs], ref, tolerance(x, wl.h, wl.rot_mode, seqs, ref), "long sampled")
     assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("Hq", [8, 64])
+def test_full_size_other_groupings_sampled(env, Hq):
+    """The full 256-sequence pool read by one query head per KV head (G = 1)
+    and by eight (G = 8): single-head kernel on a grid deeper than four rounds
+    of resident waves (first loads after the query preparation), sampled
+    against the oracle; then the first 64 sequences (a shallow grid, first
+    loads issued before the query preparation)."""
+    wl = dataclasses.replace(W.ATTN_WORKLOADS["attn"], Hq=Hq)
+    x = W.attn_inputs(wl)
+    L = x["context_lens"]
+    rng = np.random.default_rng(Hq)
+    for B in (wl.B, 64):
+        xb = dict(x, q=x["q"][:B], block_tables=x["block_tables"][:B], context_lens=L[:B])
+        maxc = int(L[:B].max())
+        say(f"attn full pool Hq={Hq} B={B} max={maxc}")
+        got = run_gpu(env, xb, maxc, wl.h, wl.rot_mode)
+        seqs = np.unique(np.r_[np.argmax(L[:B]), rng.choice(B, 3, replace=False)])
+        ref = run_oracle(xb, wl.h, wl.rot_mode, seqs=seqs)
+        check(got[seqs], ref, tolerance(xb, wl.h, wl.rot_mode, seqs, ref),
+              f"Hq={Hq} B={B} sampled")
+        assert np.all(np.isfinite(got))
