@@ -169,6 +169,21 @@ __device__ __forceinline__ bool column_hi(int n) {
 // the lower lane takes fma(a, 1, b) = f32(a + b), the upper fma(b, -1, a) =
 // f32(a - b), the same butterflies in the same order as the definition. The
 // query's reductions run over its own LQ lanes.
+// Value of lane (lane ^ m), for m a compile-time constant once unrolled:
+// DPP moves within a row of 16 lanes for m <= 8 (m = 4 as a half-row mirror,
+// lane ^ 7, followed by the quad reversal, lane ^ 3), an LDS permute beyond.
+__device__ __forceinline__ float lane_xor(float v, int m) {
+  const int b = __builtin_bit_cast(int, v);
+  int r;
+  if (m == 1) r = __builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, true);        // quad_perm 1,0,3,2
+  else if (m == 2) r = __builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, true);   // quad_perm 2,3,0,1
+  else if (m == 4) r = __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(b, 0x141, 0xF, 0xF, true),
+                                                0x1B, 0xF, 0xF, true);      // half mirror, 3,2,1,0
+  else if (m == 8) r = __builtin_amdgcn_mov_dpp(b, 0x128, 0xF, 0xF, true);  // row_ror 8
+  else return __shfl_xor(v, m);
+  return __builtin_bit_cast(float, r);
+}
+
 // The fp16 query channels of the calling lane, as loaded (CPL / 2 words).
 template <int G, bool PAIR>
 struct QueryRaw {
@@ -254,7 +269,7 @@ __device__ __forceinline__ void prepare_query(const QueryParams& p, const QueryR
         const float sg = (j & m) ? -1.0f : 1.0f;
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
-          const float xp = __shfl_xor(x[e], m);
+          const float xp = lane_xor(x[e], m);
           x[e] = __builtin_fmaf(x[e], sg, xp);
         }
       }
@@ -270,7 +285,7 @@ __device__ __forceinline__ void prepare_query(const QueryParams& p, const QueryR
     amax = fmaxf(amax, fabsf(v[e]));
   }
 #pragma unroll
-  for (int o = LQ / 2; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  for (int o = LQ / 2; o >= 1; o >>= 1) amax = fmaxf(amax, lane_xor(amax, o));
   int ex = 0;
   if (amax > 0.0f) frexpf(amax, &ex);               // amax in [2^(ex-1), 2^ex)
   const int sigma = amax > 0.0f ? 14 - ex : 0;      // max |Q| in [2^13, 2^14)
@@ -290,7 +305,7 @@ __device__ __forceinline__ void prepare_query(const QueryParams& p, const QueryR
     xs[g][j * CPL + e + 1] = q16;
   }
 #pragma unroll
-  for (int o = LQ / 2; o >= 1; o >>= 1) msum += __shfl_xor(msum, o);
+  for (int o = LQ / 2; o >= 1; o >>= 1) msum += lane_xor(msum, o);
   const float cinit_g = -8.0f * ldexpf(msum, -24);
   const float sig_g = ldexpf(1.0f, 24 - sigma);
   __syncthreads();
