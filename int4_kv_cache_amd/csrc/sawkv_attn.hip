@@ -1051,16 +1051,6 @@ __device__ __forceinline__ float quads_max(float v) {
                      __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0x12C, 0xF, 0xF, false))));
 }
 
-// Sum / max over the four rows of 16 lanes (every lane gets the result).
-__device__ __forceinline__ float rows_sum4(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
-}
-__device__ __forceinline__ float rows_max4(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
-}
-
 // QPV quads of 4 lanes per output vector: QPV = 4, one row of 16 lanes per
 // vector (4 vectors per wave), or QPV = 16, the whole wave on one vector (for
 // few vectors with many chunks). Quad qd merges chunks qd, qd + QPV, ...;
@@ -1072,11 +1062,20 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(CombineParams p) {
   const int qd = QPV == 4 ? (lane >> 2) & 3 : lane >> 2;
   const int64_t v = QPV == 4 ? (int64_t)blockIdx.x * 4 + (lane >> 4) : (int64_t)blockIdx.x;
   const bool live = v < p.n_vec;
-  const int64_t b = live ? v / p.Hq : 0;
-  const int qh = live ? (int)(v % p.Hq) : 0;
-  int L = live ? p.context_lens[b] : 0;
-  L = L < 0 ? 0 : (L > p.max_context ? p.max_context : L);
-  const int nck = (L + p.C - 1) / p.C;
+  int64_t b;
+  int qh;
+  if (p.n_vec <= (int64_t)UINT32_MAX) {
+    // 32-bit division (a 64-bit one is a long emulated sequence that would
+    // delay every load of the wave)
+    const uint32_t vv = live ? (uint32_t)v : 0u;
+    const uint32_t bb = vv / (uint32_t)p.Hq;
+    b = bb;
+    qh = (int)(vv - bb * (uint32_t)p.Hq);
+  } else {
+    b = live ? v / p.Hq : 0;
+    qh = live ? (int)(v % p.Hq) : 0;
+  }
+  const int L_raw = live ? p.context_lens[b] : 0;
   const int64_t base = b * p.NC * p.Hq + qh;      // chunk c adds c * Hq
 
   // running reference M: a chunk with a larger one rescales what is summed
@@ -1085,65 +1084,83 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(CombineParams p) {
 #pragma unroll
   for (int k = 0; k < kElems; ++k) x[k] = 0.0f;
   float lsum = 0.0f;
-  const int mine = nck > qd ? (nck - qd + QPV - 1) / QPV : 0;   // chunks qd + QPV k
-  if (mine > 0) {
-    constexpr int kDepth = 4;
-    f4_t buf[kDepth][8];
-    float2 mlb[kDepth];
-    auto fetch = [&](int k, int slot) {
-      const int64_t row = base + (int64_t)(qd + QPV * k) * p.Hq;
-      mlb[slot] = *reinterpret_cast<const float2*>(p.part_ml + row * 2);
-      const f4_t* src = reinterpret_cast<const f4_t*>(p.part_o + row * kD + 8 * lam);
+  constexpr int kDepth = 4;
+  f4_t buf[kDepth][8];
+  float2 mlb[kDepth];
+  auto fetch = [&](int k, int slot) {
+    const int64_t row = base + (int64_t)(qd + QPV * k) * p.Hq;
+    mlb[slot] = *reinterpret_cast<const float2*>(p.part_ml + row * 2);
+    const f4_t* src = reinterpret_cast<const f4_t*>(p.part_o + row * kD + 8 * lam);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        buf[slot][2 * i] = src[8 * i];
-        buf[slot][2 * i + 1] = src[8 * i + 1];
+    for (int i = 0; i < 4; ++i) {
+      buf[slot][2 * i] = src[8 * i];
+      buf[slot][2 * i + 1] = src[8 * i + 1];
+    }
+  };
+  auto accumulate = [&](int slot) {
+    const float ref = mlb[slot].x;
+    if (ref == -INFINITY) return;                 // no valid token in the chunk
+    if (ref > M) {
+      const float r = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - ref);
+      lsum *= r;
+#pragma unroll
+      for (int k = 0; k < kElems; ++k) x[k] *= r;
+      M = ref;
+    }
+    const float sc = __builtin_amdgcn_exp2f(ref - M);
+    lsum += sc * mlb[slot].y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[8 * i + j] += sc * buf[slot][2 * i][j];
+        x[8 * i + 4 + j] += sc * buf[slot][2 * i + 1][j];
       }
-    };
-    auto accumulate = [&](int slot) {
-      const float ref = mlb[slot].x;
-      if (ref == -INFINITY) return;                 // no valid token in the chunk
-      if (ref > M) {
-        const float r = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - ref);
-        lsum *= r;
-#pragma unroll
-        for (int k = 0; k < kElems; ++k) x[k] *= r;
-        M = ref;
-      }
-      const float sc = __builtin_amdgcn_exp2f(ref - M);
-      lsum += sc * mlb[slot].y;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          x[8 * i + j] += sc * buf[slot][2 * i][j];
-          x[8 * i + 4 + j] += sc * buf[slot][2 * i + 1][j];
-        }
-    };
+  };
+
+  // Quad qd merges chunks qd + QPV k, k < mine. The whole-wave form (few
+  // vectors, many chunks) loads the partials of every chunk slot of the
+  // layout without waiting for the context length, so that wait overlaps
+  // theirs; slots past the context's last chunk (not written by this call)
+  // are loaded but never merged. The 4-lane form waits for the length and
+  // loads only the chunks it merges.
+  int nfetch = 0;
+  if constexpr (QPV == 16) {
+    nfetch = p.NC > qd ? (p.NC - qd + QPV - 1) / QPV : 0;
 #pragma unroll
     for (int k = 0; k < kDepth - 1; ++k)
-      if (k < mine) fetch(k, k);
-    for (int k0 = 0; k0 < mine; k0 += kDepth) {
+      if (k < nfetch) fetch(k, k);
+    __builtin_amdgcn_sched_barrier(0);           // keep the length's wait below these loads
+  }
+  const int L = L_raw < 0 ? 0 : (L_raw > p.max_context ? p.max_context : L_raw);
+  const int nck = (L + p.C - 1) / p.C;
+  const int mine = nck > qd ? (nck - qd + QPV - 1) / QPV : 0;
+  if constexpr (QPV == 4) {
+    nfetch = mine;
 #pragma unroll
-      for (int k = 0; k < kDepth; ++k) {
-        const int kk = k0 + k;
-        if (kk >= mine) break;
-        if (kk + kDepth - 1 < mine) fetch(kk + kDepth - 1, (k + kDepth - 1) % kDepth);
-        accumulate(k);
-      }
+    for (int k = 0; k < kDepth - 1; ++k)
+      if (k < nfetch) fetch(k, k);
+  }
+  for (int k0 = 0; k0 < nfetch; k0 += kDepth) {
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) {
+      const int kk = k0 + k;
+      if (kk >= nfetch) break;
+      if (kk + kDepth - 1 < nfetch) fetch(kk + kDepth - 1, (k + kDepth - 1) % kDepth);
+      if (kk < mine) accumulate(k);
     }
   }
   // merge the quads of the vector
   float Mv = quads_max(M);
-  if constexpr (QPV == 16) Mv = rows_max4(Mv);
+  if constexpr (QPV == 16) Mv = rows_max(Mv);
   const float rq = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - Mv);
   lsum = quads_sum(lsum * rq);
 #pragma unroll
   for (int k = 0; k < kElems; ++k) x[k] = quads_sum(x[k] * rq);
   if constexpr (QPV == 16) {
-    lsum = rows_sum4(lsum);
+    lsum = rows_sum(lsum);
 #pragma unroll
-    for (int k = 0; k < kElems; ++k) x[k] = rows_sum4(x[k]);
+    for (int k = 0; k < kElems; ++k) x[k] = rows_sum(x[k]);
   }
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
 #pragma unroll
