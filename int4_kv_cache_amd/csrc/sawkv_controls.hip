@@ -125,10 +125,11 @@ template <int HB>
 __device__ __forceinline__ void gather8_tensor(const Gather8Tensor& G, const Gather8Params& p) {
   const int lane = threadIdx.x & 63;
   const int lam = lane & 3;
-  const int64_t v = (int64_t)blockIdx.x * kVecPerBlock + (threadIdx.x >> 2);
-  const bool live = v < p.TH;
-  const int64_t t = live ? v / p.H : 0;
-  const int head = live ? (int)(v - t * p.H) : 0;
+  // TH < 2^31: the vector index splits with a 32-bit division
+  const uint32_t v = blockIdx.x * (uint32_t)kVecPerBlock + (threadIdx.x >> 2);
+  const bool live = v < (uint32_t)p.TH;
+  const uint32_t t = live ? v / (uint32_t)p.H : 0u;
+  const int head = live ? (int)(v - t * (uint32_t)p.H) : 0;
   const int64_t slot = live ? p.slots[t] : -1;
   const bool valid = slot >= 0 && slot < p.n_slots;
 
@@ -165,7 +166,7 @@ __device__ __forceinline__ void gather8_tensor(const Gather8Tensor& G, const Gat
     for (int k = 0; k < kElems; ++k) o[k] = x[k] * sf;   // exact
   }
   if (live) {
-    uint4* dst = reinterpret_cast<uint4*>(G.out + v * kD + 8 * lam);
+    uint4* dst = reinterpret_cast<uint4*>(G.out + (int64_t)v * kD + 8 * lam);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint32_t wd[4];
@@ -209,8 +210,18 @@ __global__ __launch_bounds__(kThreads) void cache_append_kernel(CacheParams p) {
   if (i >= p.n_pieces) return;
   const int64_t vec = i >> 4;
   const int piece = (int)(i & 15);
-  const int64_t t = vec / p.H;
-  const int head = (int)(vec - t * p.H);
+  int64_t t;
+  int head;
+  if (p.n_pieces <= INT64_C(16) * UINT32_MAX) {
+    // 32-bit division whenever the vector index fits (a 64-bit one is a long
+    // emulated sequence ahead of the slot load)
+    const uint32_t tv = (uint32_t)vec / (uint32_t)p.H;
+    t = tv;
+    head = (int)((uint32_t)vec - tv * (uint32_t)p.H);
+  } else {
+    t = vec / p.H;
+    head = (int)(vec - t * p.H);
+  }
   const int64_t slot = p.slots[t];
   if (slot < 0 || slot >= p.n_slots) return;
   C.cache[(slot * p.H + head) * 16 + piece] = C.src[t * C.stride16 + head * 16 + piece];
