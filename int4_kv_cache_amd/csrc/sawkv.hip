@@ -370,7 +370,8 @@ __device__ __forceinline__ void gather_compute_store(const GatherTensor& G,
   }
 
   // stage the wave's 16 output rows (4 KB) through LDS, then store them as
-  // four fully contiguous 1 KB wave stores; rows padded to 272 bytes
+  // four fully contiguous 1 KB wave stores, marked nontemporal; rows padded
+  // to 272 bytes
   __shared__ uint4 stage[kWaves][kVecPerWave][17];
   const int wv = threadIdx.x >> 6, vq = (threadIdx.x & 63) >> 2;
 #pragma unroll
@@ -390,7 +391,7 @@ __device__ __forceinline__ void gather_compute_store(const GatherTensor& G,
     const int r = 4 * i + (lane >> 4), c = lane & 15;
     const uint4 w = stage[wv][r][c];
     if (v_first + r < f.TH)
-      *reinterpret_cast<uint4*>(G.out + ((int64_t)v_first + r) * kD + 8 * c) = w;
+      store_stream(w, G.out + ((int64_t)v_first + r) * kD + 8 * c);
   }
   __builtin_amdgcn_wave_barrier();
 }

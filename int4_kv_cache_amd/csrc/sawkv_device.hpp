@@ -93,6 +93,14 @@ __device__ __forceinline__ float quad_xor2(float v) {
                                                             0x4E, 0xF, 0xF, true));
 }
 
+// 16-byte store marked nontemporal (streaming output that is not read back
+// soon: it does not displace reusable lines from the caches).
+__device__ __forceinline__ void store_stream(uint4 w, void* dst) {
+  typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+  const u4v v = {w.x, w.y, w.z, w.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<u4v*>(dst));
+}
+
 // In-lane butterfly stage over register-index bit (1 << RB).
 template <int RB>
 __device__ __forceinline__ void lane_stage(float (&x)[kElems]) {
