@@ -733,7 +733,8 @@ struct PairLanes {
   const uint16_t* s_ptr;  // the lane's scale (loader role), relative to the block
 };
 
-template <bool BRANCHLESS>
+// AUX: cache policy of the code loads (0 default, 2 nontemporal).
+template <bool BRANCHLESS, int AUX>
 __device__ __forceinline__ void load_pair_step(const ChunkParams& p, StepRegs& r, int t0,
                                                int t_end, int blk0, int pages, int h0,
                                                const PairLanes& ln) {
@@ -750,10 +751,10 @@ __device__ __forceinline__ void load_pair_step(const ChunkParams& p, StepRegs& r
     const __amdgpu_buffer_rsrc_t rk = rsrc(p.k_codes + row0 * (kD / 2), reach);
     const __amdgpu_buffer_rsrc_t rv = rsrc(p.v_codes + row0 * (kD / 2), reach);
 #pragma unroll
-    for (int T = 0; T < 2; ++T) r.kq[T] = __builtin_amdgcn_raw_buffer_load_b128(rk, ln.k_off[T], 0, 0);
+    for (int T = 0; T < 2; ++T) r.kq[T] = __builtin_amdgcn_raw_buffer_load_b128(rk, ln.k_off[T], 0, AUX);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      r.vd[i >> 2][i & 3] = __builtin_amdgcn_raw_buffer_load_b32(rv, ln.v_off[i], 0, 0);
+      r.vd[i >> 2][i & 3] = __builtin_amdgcn_raw_buffer_load_b32(rv, ln.v_off[i], 0, AUX);
   } else {
 #pragma unroll
     for (int T = 0; T < 2; ++T) r.kq[T] = u4_t{0u, 0u, 0u, 0u};
@@ -881,6 +882,11 @@ __device__ __forceinline__ void compute_pair_step(const StepRegs& r, const uint3
 template <bool EARLY>
 __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
   constexpr int G = 4;
+  // Deep grids (the late-order instantiation) stream a pool far larger than
+  // the last-level cache: their code loads are nontemporal, so the stream
+  // does not displace lines that are reused. Each wave reads whole 128-byte
+  // lines (two heads' rows), so no line is shared with another wave.
+  constexpr int kAux = EARLY ? 0 : 2;
   __shared__ uint16_t sstage[64];
   __shared__ float xs[2 * G][kD];
   const int lane = threadIdx.x;
@@ -956,16 +962,16 @@ __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
   u4_t bq[4];
   float cinit, F;
   if constexpr (EARLY) {
-    load_pair_step<true>(p, cur, t_begin, t_end, blk0, pages, h0, ln);
+    load_pair_step<true, kAux>(p, cur, t_begin, t_end, blk0, pages, h0, ln);
     prepare_query<G, true>(p.qp, qraw, lane, xs, bq, cinit, F);
   } else {
     prepare_query<G, true>(p.qp, qraw, lane, xs, bq, cinit, F);
-    load_pair_step<false>(p, cur, t_begin, t_end, blk0, pages, h0, ln);
+    load_pair_step<false, kAux>(p, cur, t_begin, t_end, blk0, pages, h0, ln);
   }
   const float F4 = 4.0f * F;
   for (int t0 = t_begin; t0 < t_end; t0 += 16) {
     const int t1 = t0 + 16;
-    if (t1 < t_end) load_pair_step<false>(p, nxt, t1, t_end, blk0, pages, h0, ln);
+    if (t1 < t_end) load_pair_step<false, kAux>(p, nxt, t1, t_end, blk0, pages, h0, ln);
     sstage[lane] = (uint16_t)cur.sc;
     __builtin_amdgcn_wave_barrier();
     uint32_t ks[2][2], vs[2][2];
@@ -1278,7 +1284,8 @@ const void* const kChunkPair[2] = {(void*)&attn_chunk_pair_kernel<false>,
 // compute units) issues each wave's first loads before its query
 // preparation: few rounds leave that latency on the critical path. Deeper
 // grids hide it behind other waves, and there the early loads measured
-// slightly slower.
+// slightly slower; the head-pair kernel's deep-grid instantiation also reads
+// the codes with nontemporal loads.
 constexpr int64_t kEarlyIssueBlocks = 4 * 3 * 4 * 256;
 const void* const kCombine[2][5] = {
     {(void*)&attn_combine_kernel<0, 4>, (void*)&attn_combine_kernel<16, 4>,
