@@ -318,3 +318,27 @@ def test_full_size_other_groupings_sampled(env, Hq):
         check(got[seqs], ref, tolerance(xb, wl.h, wl.rot_mode, seqs, ref),
               f"Hq={Hq} B={B} sampled")
         assert np.all(np.isfinite(got))
+
+
+def test_workspace_reused_with_shorter_contexts(env):
+    """One workspace for two calls: the first over long contexts fills every
+    chunk slot with partials, the second over shorter contexts of the same
+    layout (same B and max_context) must merge only its own chunks, not the
+    first call's partials left in the slots past its contexts' ends."""
+    torch, S = env
+    wl = small(B=4, ctx=("list", (6000, 5990, 6000, 5000)), wid=41, masked=0)
+    x = W.attn_inputs(wl)
+    d = to_dev(env, x)
+    pools = (d["k_codes"], d["v_codes"], d["k_scales"], d["v_scales"])
+    ws = torch.empty(S.attention_workspace_size(wl.B, wl.Hq, wl.H, 6000), dtype=torch.uint8,
+                     device="cuda")
+    for lens in ((6000, 5990, 6000, 5000), (700, 0, 2500, 17)):
+        L = np.array(lens, dtype=np.int32)
+        say(f"attn workspace reuse, contexts {lens}")
+        got = S.decode_attention(d["q"], pools, d["block_tables"], torch.from_numpy(L).cuda(),
+                                 6000, h=wl.h, rot="kv", workspace=ws)
+        torch.cuda.synchronize()
+        xb = dict(x, context_lens=L)
+        ref = run_oracle(xb, wl.h, O.ROT_KV)
+        check(got.cpu().numpy(), ref, tolerance(xb, wl.h, O.ROT_KV, np.arange(wl.B), ref),
+              f"reuse {lens}")
