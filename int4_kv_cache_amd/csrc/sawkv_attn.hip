@@ -879,14 +879,14 @@ __device__ __forceinline__ void compute_pair_step(const StepRegs& r, const uint3
   }
 }
 
-template <bool EARLY>
+template <bool EARLY, bool STREAM>
 __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
   constexpr int G = 4;
-  // Deep grids (the late-order instantiation) stream a pool far larger than
-  // the last-level cache: their code loads are nontemporal, so the stream
-  // does not displace lines that are reused. Each wave reads whole 128-byte
-  // lines (two heads' rows), so no line is shared with another wave.
-  constexpr int kAux = EARLY ? 0 : 2;
+  // STREAM: the call reads a pool several times larger than the last-level
+  // cache, so the code loads are nontemporal and the stream does not displace
+  // lines that are reused. Each wave reads whole 128-byte lines (two heads'
+  // rows), so no line is shared with another wave.
+  constexpr int kAux = STREAM ? 2 : 0;
   __shared__ uint16_t sstage[64];
   __shared__ float xs[2 * G][kD];
   const int lane = threadIdx.x;
@@ -1277,16 +1277,26 @@ const void* const kChunk[2][4] = {
      (void*)&attn_chunk_kernel<4, false>, (void*)&attn_chunk_kernel<8, false>},
     {(void*)&attn_chunk_kernel<1, true>, (void*)&attn_chunk_kernel<2, true>,
      (void*)&attn_chunk_kernel<4, true>, (void*)&attn_chunk_kernel<8, true>}};
-const void* const kChunkPair[2] = {(void*)&attn_chunk_pair_kernel<false>,
-                                   (void*)&attn_chunk_pair_kernel<true>};
+// [first-step order][nontemporal code loads]
+const void* const kChunkPair[2][2] = {
+    {(void*)&attn_chunk_pair_kernel<false, false>, (void*)&attn_chunk_pair_kernel<false, true>},
+    {(void*)&attn_chunk_pair_kernel<true, false>, (void*)&attn_chunk_pair_kernel<true, true>}};
 
 // A grid of at most four rounds of resident chunk waves (3 per SIMD on 256
 // compute units) issues each wave's first loads before its query
 // preparation: few rounds leave that latency on the critical path. Deeper
 // grids hide it behind other waves, and there the early loads measured
-// slightly slower; the head-pair kernel's deep-grid instantiation also reads
-// the codes with nontemporal loads.
+// slightly slower.
 constexpr int64_t kEarlyIssueBlocks = 4 * 3 * 4 * 256;
+
+// The head-pair kernel reads the codes with nontemporal loads when the
+// contexts the call may read (B x max_context tokens, 132 bytes per token and
+// KV head for K and V codes and scales) exceed three times the 256 MB
+// last-level cache: such a pool cannot stay cached between calls anyway, and
+// streaming it past the cache measured 3-7 % faster from 96 sequences up.
+// Smaller pools keep ordinary loads (64 sequences: 4.7 % slower with
+// nontemporal loads, back to back).
+constexpr double kStreamPoolBytes = 3.0 * 256.0 * 1024.0 * 1024.0;
 const void* const kCombine[2][5] = {
     {(void*)&attn_combine_kernel<0, 4>, (void*)&attn_combine_kernel<16, 4>,
      (void*)&attn_combine_kernel<32, 4>, (void*)&attn_combine_kernel<64, 4>,
@@ -1376,9 +1386,10 @@ int attention_impl(const void* q, int64_t q_stride, const void* k_codes, const v
   cp.n_groups = (uint32_t)(B * lay.NC);
   const int64_t chunk_blocks = ((B * lay.NC + 7) / 8) * 8 * groups;
   const int early = chunk_blocks <= kEarlyIssueBlocks ? 1 : 0;
+  const bool streamed = (double)B * (double)max_context * (double)H * 132.0 > kStreamPoolBytes;
   if (max_context > 0 &&
-      (st = launch64(pair ? kChunkPair[early] : kChunk[early][g_index(G)], chunk_blocks, &cp,
-                     s)))
+      (st = launch64(pair ? kChunkPair[early][streamed ? 1 : 0] : kChunk[early][g_index(G)],
+                     chunk_blocks, &cp, s)))
     return st;
 
   sawkv::attn::CombineParams mp{};
