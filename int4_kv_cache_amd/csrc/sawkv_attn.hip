@@ -157,18 +157,6 @@ __device__ __forceinline__ bool column_hi(int n) {
   else return n < G;
 }
 
-// The B operand of the score MFMAs for the calling lane (bq), and for the
-// lane's column n = lane % 16 the accumulator start value (minus 8 times the
-// sum of the query's effective multipliers, cinit) and the log2-unit scale F.
-// The wave's queries are those of head group `hg` of sequence b: one KV head,
-// or a pair of KV heads (PAIR). xs: NQ x 128 floats of LDS. One wave.
-//
-// Query g of the wave is held by LQ = 64 / NQ consecutive lanes, CPL = 2 NQ
-// contiguous channels per lane, so the Walsh-Hadamard stages of stride < CPL
-// are in-lane and the others pair lane j of the query with lane j ^ (s / CPL):
-// the lower lane takes fma(a, 1, b) = f32(a + b), the upper fma(b, -1, a) =
-// f32(a - b), the same butterflies in the same order as the definition. The
-// query's reductions run over its own LQ lanes.
 // Value of lane (lane ^ m), for m a compile-time constant once unrolled:
 // DPP moves within a row of 16 lanes for m <= 8 (m = 4 as a half-row mirror,
 // lane ^ 7, followed by the quad reversal, lane ^ 3), an LDS permute beyond.
