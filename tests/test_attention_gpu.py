@@ -269,17 +269,23 @@ def test_append_then_attention(env):
 # full size: 256 sequences, contexts up to 8000, sampled against the oracle
 # --------------------------------------------------------------------------
 
-def test_full_size_sampled(env):
+# 256 sequences: a deep grid with nontemporal code loads; 128: a shallow grid
+# (first loads before the query preparation) whose pool is still streamed
+@pytest.mark.parametrize("B", [256, 128])
+def test_full_size_sampled(env, B):
     wl = W.ATTN_WORKLOADS["attn"]
     x = W.attn_inputs(wl)
+    if B < wl.B:
+        x = dict(x, q=x["q"][:B], block_tables=x["block_tables"][:B],
+                 context_lens=x["context_lens"][:B])
     L = x["context_lens"]
     maxc = int(L.max())
-    say(f"attn full size B={wl.B} tokens={int(L.sum())} max={maxc}")
+    say(f"attn full size B={B} tokens={int(L.sum())} max={maxc}")
     got = run_gpu(env, x, maxc, wl.h, wl.rot_mode)
-    rng = np.random.default_rng(0)
-    seqs = np.unique(np.r_[np.argmin(L), np.argmax(L), rng.choice(wl.B, 4, replace=False)])
+    rng = np.random.default_rng(B)
+    seqs = np.unique(np.r_[np.argmin(L), np.argmax(L), rng.choice(B, 4, replace=False)])
     ref = run_oracle(x, wl.h, wl.rot_mode, seqs=seqs)
-    check(got[seqs], ref, tolerance(x, wl.h, wl.rot_mode, seqs, ref), "full sampled")
+    check(got[seqs], ref, tolerance(x, wl.h, wl.rot_mode, seqs, ref), f"full sampled B={B}")
     assert np.all(np.isfinite(got))
 
 
