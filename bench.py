@@ -240,10 +240,12 @@ def controls(S, torch, wl, kv, slots, timed, stream, h, rot):
     return res
 
 
-def decode_extras(torch, step_rot, timed, stream, wl, layers):
-    """For comparison with the one-launch step: one call per layer (eager),
-    and the same per-layer calls replayed from one HIP graph."""
+def decode_extras(torch, step_rot, timed, stream, wl, layers, step_prepared):
+    """For comparison with the one-launch step: one call per layer (eager,
+    through the checking binding and through prepared calls that only
+    launch), and the same per-layer calls replayed from one HIP graph."""
     eager_ms = timed(step_rot, 200)
+    prepared_ms = timed(step_prepared, 200)
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(stream)
@@ -266,6 +268,8 @@ def decode_extras(torch, step_rot, timed, stream, wl, layers):
     return {"layer_calls_per_step": layers,
             "eager_us_per_step": round(eager_ms * 1e3, 2),
             "eager_us_per_layer_call": round(eager_ms * 1e3 / layers, 3),
+            "prepared_us_per_step": round(prepared_ms * 1e3, 2),
+            "prepared_us_per_layer_call": round(prepared_ms * 1e3 / layers, 3),
             "graph_us_per_step": round(graph_ms * 1e3, 2),
             "graph_us_per_layer_call": round(graph_ms * 1e3 / layers, 3),
             "graph_tokens_per_s": round(wl.T / (graph_ms * 1e-3), 1)}
@@ -690,7 +694,14 @@ def main():
     if args.workload == "sweep":
         extra["variants"] = sweep_variants(S, torch, wl, kvs[0], slots, timed, stream)
     if args.workload == "decode":
-        extra["decode"] = decode_extras(torch, per_layer_rot, timed, stream, wl, layers)
+        prepared = [S.AppendCall(kvs[layer][0], kvs[layer][1], slots, *pools[layer], h=h,
+                                 rot=ROT_NAME[rot]) for layer in range(layers)]
+
+        def per_layer_prepared():
+            for call in prepared:
+                call()
+        extra["decode"] = decode_extras(torch, per_layer_rot, timed, stream, wl, layers,
+                                        per_layer_prepared)
     if args.workload in ("sweep", "long", "prefill"):
         ko, vo = outs[0]
         extra["mse"] = {"k": mse_gpu(torch, ko, kvs[0][0]), "v": mse_gpu(torch, vo, kvs[0][1])}

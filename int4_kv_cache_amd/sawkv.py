@@ -135,10 +135,7 @@ def alloc_pools(N_pg, P, H, D, device="cuda", code_fill=None, scale_bits_fill=No
     return kc, vc, ks, vs
 
 
-def quantize_append(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, *,
-                    h=128, rot="kv", stream=None):
-    """Fused rotate + token-wise INT4 + paged append (sawkv_quantize_append).
-    k or v may be None to skip that tensor."""
+def _append_args(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, h, rot):
     ref = k if k is not None else v
     T, H, D, _ = _kv_geometry(ref)
     ks_ = _kv_geometry(k)[3] if k is not None else 0
@@ -148,11 +145,34 @@ def quantize_append(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, *,
     N_pg, P = pool[0], pool[1]
     if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T:
         raise ValueError("slot_mapping must be int64 [T]")
-    _check(lib.sawkv_quantize_append(
-        _addr(k), _addr(v), ks_, vs_, _addr(slot_mapping), T, H, D,
-        _addr(k_codes) if k is not None else None, _addr(v_codes) if v is not None else None,
-        _addr(k_scales) if k is not None else None, _addr(v_scales) if v is not None else None,
-        N_pg, P, h, _rot(rot), _stream(stream)))
+    return (_addr(k), _addr(v), ks_, vs_, _addr(slot_mapping), T, H, D,
+            _addr(k_codes) if k is not None else None, _addr(v_codes) if v is not None else None,
+            _addr(k_scales) if k is not None else None, _addr(v_scales) if v is not None else None,
+            N_pg, P, h, _rot(rot))
+
+
+def quantize_append(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, *,
+                    h=128, rot="kv", stream=None):
+    """Fused rotate + token-wise INT4 + paged append (sawkv_quantize_append).
+    k or v may be None to skip that tensor."""
+    args = _append_args(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, h, rot)
+    _check(lib.sawkv_quantize_append(*args, _stream(stream)))
+
+
+class AppendCall:
+    """sawkv_quantize_append with its arguments checked and marshalled once:
+    calling the object only launches (for loops of per-layer calls, where the
+    per-call Python checks would otherwise exceed the kernel time). The
+    tensors must stay alive and keep their storage while the object is used."""
+
+    def __init__(self, k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, *, h=128,
+                 rot="kv"):
+        self._args = _append_args(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales,
+                                  h, rot)
+        self._keep = (k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales)
+
+    def __call__(self, stream=None):
+        _check(lib.sawkv_quantize_append(*self._args, _stream(stream)))
 
 
 def quantize_append_layers(kv, slot_mapping, pools, *, h=128, rot="kv", stream=None):

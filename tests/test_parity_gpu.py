@@ -283,6 +283,26 @@ def test_naive_entry_points_match_rot_none(env):
     assert_pools_equal([to_np(x) for x in a], want, "naive")
 
 
+def test_prepared_append_call_matches_oracle(env):
+    """AppendCall (arguments checked once, then launch only) writes what the
+    oracle writes, on every call, including K-only rotation."""
+    torch, S = env
+    wl = W.WORKLOADS["sweep"]
+    k, v = W.kv(wl, 0, 0, 512)
+    slots = W.slot_mapping(wl)[:512].copy()
+    kd, vd, sd = (torch.from_numpy(a).cuda() for a in (k, v, slots))
+    for rot, orot in (("kv", O.ROT_KV), ("k", O.ROT_K)):
+        say(f"prepared append call rot={rot}")
+        gp = gpu_pools(env, wl.N_pg, wl.P, wl.H, wl.D)
+        call = S.AppendCall(kd, vd, sd, *gp, h=128, rot=rot)
+        for _ in range(2):
+            call()
+        torch.cuda.synchronize()
+        want = np_pools(wl.N_pg, wl.P, wl.H, wl.D)
+        O.quantize_append(k, v, slots, *want, h=128, rot_mode=orot)
+        assert_pools_equal([to_np(x) for x in gp], want, f"prepared rot={rot}")
+
+
 def test_zero_tokens_is_a_no_op(env):
     torch, S = env
     gp = gpu_pools(env, 2, 16, 8, 128)
