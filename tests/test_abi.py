@@ -280,6 +280,26 @@ def test_attention_workspace_size(lib):
     assert b"workspace" in lib.sawkv_last_error()
 
 
+@pytest.mark.parametrize("B,H,maxc,C", [
+    (256, 8, 8000, 1024),   # 16384 (sequence, chunk, head) items at 1024 tokens
+    (64, 8, 32768, 1024),   # long contexts: 16384 items at 1024
+    (192, 8, 8000, 512),    # 12288 items at 1024: 512-token chunks
+    (16, 8, 8000, 128),     # halved while fewer than 8192 items, down to 128
+    (1, 8, 3611, 64),       # fewer than 1024 items even at 128: 64-token chunks
+])
+def test_attention_workspace_follows_the_chunk_rule(lib, B, H, maxc, C):
+    """The workspace holds float32 partials per (sequence, chunk, query head):
+    a (max, sum) pair and a 128-channel output, each region 256-byte aligned;
+    the chunk count is ceil(max_context / C) for the chunk length C the
+    launch picks from the step's size."""
+    Hq = 4 * H
+    st, n = attn_ws(lib, B=B, Hq=Hq, H=H, maxc=maxc)
+    assert st == OK
+    nc = -(-maxc // C)
+    align = lambda x: (x + 255) // 256 * 256
+    assert n == align(B * nc * Hq * 2 * 4) + align(B * nc * Hq * 128 * 4)
+
+
 # ---- controls: uncompressed cache write and token-wise INT8 (validation only) ----
 
 def ctl(lib, name, **kw):
