@@ -198,12 +198,19 @@ static_assert(sizeof(LayersParams) <= 4096, "kernel arguments must stay within 4
 
 template <int HB0, int HB1>
 __global__ __launch_bounds__(kThreads) void append_layers_kernel(LayersParams p) {
-  // tensor-major: every layer's first tensor (K, the rotated one under
-  // K-only rotation) is dispatched before any second tensor, so in a launch
+  // blockIdx.y = layer, blockIdx.z = tensor of the layer. Dispatch runs x,
+  // then y, then z, so every layer's first tensor (K, the rotated one under
+  // K-only rotation) is dispatched before any second tensor, and in a launch
   // of one round of waves the data that arrives last feeds the shorter
-  // (unrotated) arithmetic
-  const int slot_in_layer = (int)(blockIdx.y / (unsigned)p.n_layers);
-  const LayerPtrs& L = p.layer[blockIdx.y % (unsigned)p.n_layers];
+  // (unrotated) arithmetic. The layer's pointers are addressed by blockIdx.y
+  // alone, so their argument loads go out with the first ones.
+  const int slot_in_layer = (int)blockIdx.z;
+  const LayerPtrs& L = p.layer[blockIdx.y];
+  // every argument the wave needs, in one round of scalar loads
+  asm volatile("" ::"s"(L.k), "s"(L.v), "s"(L.k_codes), "s"(L.v_codes), "s"(L.k_scales),
+               "s"(L.v_scales), "s"(p.k_stride), "s"(p.v_stride), "s"(p.n_tensors),
+               "s"(p.only_v), "s"(p.common.slots), "s"(p.common.n_slots), "s"(p.common.T),
+               "s"(p.common.TH), "s"(p.common.H), "s"(p.common.h_magic));
   const bool is_v = p.n_tensors == 2 ? slot_in_layer == 1 : p.only_v != 0;
   const AppendTensor A = is_v ? AppendTensor{L.v, p.v_stride, L.v_codes, L.v_scales}
                               : AppendTensor{L.k, p.k_stride, L.k_codes, L.k_scales};
@@ -522,9 +529,10 @@ unsigned gather_blocks(int32_t TH) {
   return (unsigned)((TH + sawkv::kVecPerBlock - 1) / sawkv::kVecPerBlock);
 }
 
-int launch(const void* fn, int grid_y, unsigned blocks, void* params, void* stream) {
+int launch(const void* fn, int grid_y, unsigned blocks, void* params, void* stream,
+           int grid_z = 1) {
   if (fn == nullptr) return fail(SAWKV_EINVAL, "no kernel for this tensor/rotation combination");
-  const dim3 grid(blocks, (unsigned)grid_y);
+  const dim3 grid(blocks, (unsigned)grid_y, (unsigned)grid_z);
   void* args[] = {params};
   const hipError_t e = hipLaunchKernel(fn, grid, dim3(sawkv::kThreads), args, 0,
                                        reinterpret_cast<hipStream_t>(stream));
@@ -609,8 +617,9 @@ int append_layers_impl(const sawkv_layer_t* layers, int32_t n_layers, int64_t k_
   p.common.TH = (int32_t)(T * H);
   p.common.H = H;
   p.common.h_magic = (uint32_t)(((1u << 20) + (uint32_t)H - 1u) / (uint32_t)H);
-  return launch(kAppendLayers[hb[0]][hb[1]], n * n_layers, append_blocks(p.common.TH), &p,
-                stream);
+  // grid (blocks, layers, tensors per layer)
+  return launch(kAppendLayers[hb[0]][hb[1]], n_layers, append_blocks(p.common.TH), &p, stream,
+                n);
 }
 
 int gather_impl(const void* k_codes, const void* v_codes, const void* k_scales,
