@@ -253,6 +253,10 @@ int sawkv_int8_gather(const void* k_codes, const void* v_codes,
  *                 entries past a sequence's last page are never read
  *   context_lens  int32 [B], device memory; values above max_context are
  *                 cut to max_context, negative values count as 0
+ *   max_context   also sizes the split of the contexts into chunks and
+ *                 decides whether the pool is streamed past the cache
+ *                 (B x max_context x H x 132 bytes above 768 MiB): pass the
+ *                 batch's longest context, not a loose capacity bound
  *   out           fp16 [B][Hq][D] contiguous
  *   workspace     device memory of at least the size that
  *                 sawkv_decode_attention_workspace_size reports for the same
