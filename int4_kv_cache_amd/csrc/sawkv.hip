@@ -474,14 +474,21 @@ int check_tensor(const char* name, const void* x, int64_t stride, const void* co
     return fail(SAWKV_EINVAL, "%s pool pointer is NULL", name);
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 16))
     return fail(SAWKV_EALIGN, "%s tensor or pool pointer not 16-byte aligned", name);
-  if (stride >= 0) {
-    if (stride < (int64_t)H * D)
-      return fail(SAWKV_EINVAL, "%s stride %lld < H*D = %d", name, (long long)stride, H * D);
-    if (stride % 8 != 0)
-      return fail(SAWKV_EALIGN, "%s stride %lld not a multiple of 8", name, (long long)stride);
-    if (stride >= (INT64_C(1) << 26))
-      return fail(SAWKV_EUNSUPPORTED, "%s stride %lld too large (< 2^26)", name, (long long)stride);
-  }
+  // a negative stride is below H*D too, so it is rejected here
+  if (stride < (int64_t)H * D)
+    return fail(SAWKV_EINVAL, "%s stride %lld < H*D = %d", name, (long long)stride, H * D);
+  if (stride % 8 != 0)
+    return fail(SAWKV_EALIGN, "%s stride %lld not a multiple of 8", name, (long long)stride);
+  if (stride >= (INT64_C(1) << 26))
+    return fail(SAWKV_EUNSUPPORTED, "%s stride %lld too large (< 2^26)", name, (long long)stride);
+  return SAWKV_OK;
+}
+
+int check_output(const char* name, const void* out, const void* codes, const void* scales) {
+  if (codes == nullptr || scales == nullptr)
+    return fail(SAWKV_EINVAL, "%s pool pointer is NULL", name);
+  if (!aligned(out, 16) || !aligned(codes, 16) || !aligned(scales, 16))
+    return fail(SAWKV_EALIGN, "%s output or pool pointer not 16-byte aligned", name);
   return SAWKV_OK;
 }
 
@@ -498,6 +505,7 @@ namespace {
 
 using sawkv::host::aligned;
 using sawkv::host::check_geometry;
+using sawkv::host::check_output;
 using sawkv::host::check_tensor;
 using sawkv::host::fail;
 using sawkv::host::g_err;
@@ -524,7 +532,7 @@ unsigned append_blocks(int32_t TH) {
   return (unsigned)((TH + sawkv::kVecPerBlock - 1) / sawkv::kVecPerBlock);
 }
 
-// One gather block = 4 waves x 2 batches = 128 vectors of one tensor.
+// One gather block = 4 waves x 16 vectors = 64 vectors of one tensor.
 unsigned gather_blocks(int32_t TH) {
   return (unsigned)((TH + sawkv::kVecPerBlock - 1) / sawkv::kVecPerBlock);
 }
@@ -630,8 +638,8 @@ int gather_impl(const void* k_codes, const void* v_codes, const void* k_scales,
   if (st) return st;
   if (T == 0) return ok();
   if (k_out == nullptr && v_out == nullptr) return fail(SAWKV_EINVAL, "both outputs are NULL");
-  if (k_out && (st = check_tensor("k", k_out, -1, k_codes, k_scales, H, D))) return st;
-  if (v_out && (st = check_tensor("v", v_out, -1, v_codes, v_scales, H, D))) return st;
+  if (k_out && (st = check_output("k", k_out, k_codes, k_scales))) return st;
+  if (v_out && (st = check_output("v", v_out, v_codes, v_scales))) return st;
 
   sawkv::GatherParams p{};
   int n = 0, hb[2] = {0, 0};

@@ -238,6 +238,7 @@ namespace {
 
 using sawkv::host::aligned;
 using sawkv::host::check_geometry;
+using sawkv::host::check_output;
 using sawkv::host::check_tensor;
 using sawkv::host::fail;
 using sawkv::host::hb_index;
@@ -307,8 +308,8 @@ int int8_gather_impl(const void* k_codes, const void* v_codes, const void* k_sca
   if (st) return st;
   if (T == 0) return ok();
   if (k_out == nullptr && v_out == nullptr) return fail(SAWKV_EINVAL, "both outputs are NULL");
-  if (k_out && (st = check_tensor("k", k_out, -1, k_codes, k_scales, H, D))) return st;
-  if (v_out && (st = check_tensor("v", v_out, -1, v_codes, v_scales, H, D))) return st;
+  if (k_out && (st = check_output("k", k_out, k_codes, k_scales))) return st;
+  if (v_out && (st = check_output("v", v_out, v_codes, v_scales))) return st;
   sawkv::controls::Gather8Params p{};
   int n = 0, hb[2] = {0, 0};
   if (k_out) {

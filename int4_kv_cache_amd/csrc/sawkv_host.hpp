@@ -22,8 +22,13 @@ bool aligned(const void* p, uintptr_t a);
 // detail text.
 int check_geometry(int64_t T, int32_t H, int32_t D, int64_t N_pg, int32_t P, int32_t h,
                    int32_t rot_mode, const int64_t* slots);
+// Input tensor: stride (elements between tokens) must be in [H*D, 2^26) and a
+// multiple of 8; pointers 16-byte aligned, pool pointers non-null.
 int check_tensor(const char* name, const void* x, int64_t stride, const void* codes,
                  const void* scales, int32_t H, int32_t D);
+// Contiguous output rows of a read-back: pointers 16-byte aligned, pool
+// pointers non-null.
+int check_output(const char* name, const void* out, const void* codes, const void* scales);
 
 // Kernel-table index of a tensor: 0 = not rotated, 1..4 = h 16/32/64/128.
 int hb_index(int32_t h, bool rot);

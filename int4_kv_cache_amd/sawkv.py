@@ -120,6 +120,45 @@ def _pool_geometry(codes, scales):
     return codes.shape
 
 
+def _on_gpu(*tensors):
+    """Every tensor handed to the library must live in device memory of one GPU."""
+    devs = {t.device for t in tensors if t is not None}
+    if any(d.type != "cuda" for d in devs):
+        raise ValueError("every tensor must be on the GPU (device memory)")
+    if len(devs) > 1:
+        raise ValueError(f"tensors are on different devices: {sorted(map(str, devs))}")
+
+
+def _pools_for(H, D, pairs):
+    """Geometry (N_pg, P, H, D/2) shared by every present (codes, scales) pair;
+    each pool's heads and row width must be those of the K/V rows it holds."""
+    shape = None
+    for codes, scales in pairs:
+        g = tuple(_pool_geometry(codes, scales))
+        if g[2:] != (H, D // 2):
+            raise ValueError(f"pool [N_pg, P, H, D/2] = {list(g)} does not hold rows of "
+                             f"H={H} heads x D={D}")
+        if shape is not None and g != shape:
+            raise ValueError(f"K and V pools differ in shape: {list(shape)} vs {list(g)}")
+        shape = g
+    if shape is None:
+        raise ValueError("no pool given")
+    return shape
+
+
+def _kv_pair(k, v):
+    """(T, H, D, k token stride, v token stride) of the present K/V tensors,
+    which must agree in T, H and D."""
+    if k is None and v is None:
+        raise ValueError("k and v are both None")
+    gk = _kv_geometry(k) if k is not None else None
+    gv = _kv_geometry(v) if v is not None else None
+    if gk is not None and gv is not None and gk[:3] != gv[:3]:
+        raise ValueError(f"K {list(gk[:3])} and V {list(gv[:3])} differ in [T, H, D]")
+    T, H, D = (gk or gv)[:3]
+    return T, H, D, gk[3] if gk else 0, gv[3] if gv else 0
+
+
 def alloc_pools(N_pg, P, H, D, device="cuda", code_fill=None, scale_bits_fill=None):
     """The four pool tensors (K codes, V codes, K scales, V scales)."""
     kc = torch.empty((N_pg, P, H, D // 2), dtype=torch.uint8, device=device)
@@ -135,16 +174,18 @@ def alloc_pools(N_pg, P, H, D, device="cuda", code_fill=None, scale_bits_fill=No
     return kc, vc, ks, vs
 
 
+def _present_pools(k, v, k_codes, v_codes, k_scales, v_scales):
+    return [pair for x, pair in ((k, (k_codes, k_scales)), (v, (v_codes, v_scales)))
+            if x is not None]
+
+
 def _append_args(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, h, rot):
-    ref = k if k is not None else v
-    T, H, D, _ = _kv_geometry(ref)
-    ks_ = _kv_geometry(k)[3] if k is not None else 0
-    vs_ = _kv_geometry(v)[3] if v is not None else 0
-    pool = _pool_geometry(k_codes, k_scales) if k is not None else \
-        _pool_geometry(v_codes, v_scales)
-    N_pg, P = pool[0], pool[1]
+    T, H, D, ks_, vs_ = _kv_pair(k, v)
+    pairs = _present_pools(k, v, k_codes, v_codes, k_scales, v_scales)
+    N_pg, P = _pools_for(H, D, pairs)[:2]
     if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T:
         raise ValueError("slot_mapping must be int64 [T]")
+    _on_gpu(k, v, slot_mapping, *[t for pair in pairs for t in pair])
     return (_addr(k), _addr(v), ks_, vs_, _addr(slot_mapping), T, H, D,
             _addr(k_codes) if k is not None else None, _addr(v_codes) if v is not None else None,
             _addr(k_scales) if k is not None else None, _addr(v_scales) if v is not None else None,
@@ -204,12 +245,8 @@ def _layers_args(kv, slot_mapping, pools, h, rot):
     if n != len(pools) or not 1 <= n <= MAX_LAYERS:
         raise ValueError(f"need 1..{MAX_LAYERS} layers with one pool set each")
     k0, v0 = kv[0]
-    ref = k0 if k0 is not None else v0
-    T, H, D, _ = _kv_geometry(ref)
-    ks_ = _kv_geometry(k0)[3] if k0 is not None else 0
-    vs_ = _kv_geometry(v0)[3] if v0 is not None else 0
-    pool = _pool_geometry(pools[0][0], pools[0][2]) if k0 is not None else \
-        _pool_geometry(pools[0][1], pools[0][3])
+    T, H, D, ks_, vs_ = _kv_pair(k0, v0)
+    pool = _pools_for(H, D, _present_pools(k0, v0, *pools[0]))
     if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T:
         raise ValueError("slot_mapping must be int64 [T]")
     descs = (LayerDesc * n)()
@@ -220,43 +257,38 @@ def _layers_args(kv, slot_mapping, pools, h, rot):
         for x, stride in ((k, ks_), (v, vs_)):
             if x is not None and _kv_geometry(x) != (T, H, D, stride):
                 raise ValueError("every layer must have the same [T, H, D] and stride")
-        for codes, scales, present in ((kc, kss, k is not None), (vc, vss, v is not None)):
-            if present and tuple(_pool_geometry(codes, scales)) != tuple(pool):
-                raise ValueError("every layer's pools must have the same shape")
+        if _pools_for(H, D, _present_pools(k, v, kc, vc, kss, vss)) != pool:
+            raise ValueError("every layer's pools must have the same shape")
         descs[i] = LayerDesc(_addr(k), _addr(v),
                              _addr(kc) if k is not None else None,
                              _addr(vc) if v is not None else None,
                              _addr(kss) if k is not None else None,
                              _addr(vss) if v is not None else None)
+    _on_gpu(slot_mapping, *[x for layer in kv for x in layer],
+            *[t for layer_pools in pools for t in layer_pools])
     return (descs, n, ks_, vs_, _addr(slot_mapping), T, H, D, pool[0], pool[1], h, _rot(rot))
 
 
 def naive_int4_append(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, *,
                       stream=None):
     """The no-rotation control (sawkv_naive_int4_append)."""
-    ref = k if k is not None else v
-    T, H, D, _ = _kv_geometry(ref)
-    ks_ = _kv_geometry(k)[3] if k is not None else 0
-    vs_ = _kv_geometry(v)[3] if v is not None else 0
-    pool = _pool_geometry(k_codes, k_scales) if k is not None else \
-        _pool_geometry(v_codes, v_scales)
-    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T:
-        raise ValueError("slot_mapping must be int64 [T]")
-    _check(lib.sawkv_naive_int4_append(
-        _addr(k), _addr(v), ks_, vs_, _addr(slot_mapping), T, H, D,
-        _addr(k_codes) if k is not None else None, _addr(v_codes) if v is not None else None,
-        _addr(k_scales) if k is not None else None, _addr(v_scales) if v is not None else None,
-        pool[0], pool[1], _stream(stream)))
+    a = _append_args(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, 128, "none")
+    _check(lib.sawkv_naive_int4_append(*a[:14], _stream(stream)))
 
 
 def _gather_args(k_codes, v_codes, k_scales, v_scales, slot_mapping, k_out, v_out, want_k,
                  want_v):
-    pool = _pool_geometry(k_codes, k_scales) if want_k else _pool_geometry(v_codes, v_scales)
-    N_pg, P, H, half = pool
+    if not (want_k or want_v):
+        raise ValueError("neither K nor V wanted")
+    pairs = [pair for want, pair in ((want_k, (k_codes, k_scales)), (want_v, (v_codes, v_scales)))
+             if want]
+    H, half = _pool_geometry(*pairs[0])[2:]
+    N_pg, P, H, half = _pools_for(H, 2 * half, pairs)
     D = 2 * half
     T = slot_mapping.numel()
-    if slot_mapping.dtype != torch.int64:
+    if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1:
         raise ValueError("slot_mapping must be int64 [T]")
+    _on_gpu(slot_mapping, k_out, v_out, *[t for pair in pairs for t in pair])
     dev = (k_codes if want_k else v_codes).device
     if want_k and k_out is None:
         k_out = torch.empty((T, H, D), dtype=torch.float16, device=dev)
@@ -308,6 +340,7 @@ def _attention_args(q, pools, block_tables, context_lens, max_context, h, rot, s
     if tuple(_pool_geometry(v_codes, v_scales)) != (N_pg, P, H, half):
         raise ValueError("K and V pools must have the same shape")
     D = 2 * half
+    _on_gpu(q, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens, out, workspace)
     if q.dtype != torch.float16 or q.dim() != 3 or q.shape[2] != D or q.stride(2) != 1 \
             or (q.shape[1] > 1 and q.stride(1) != D):
         raise ValueError("q must be fp16 [B, Hq, D] with unit channel stride and head stride D")
@@ -380,6 +413,22 @@ def _int8_pool_geometry(codes, scales):
     return codes.shape
 
 
+def _int8_pools_for(H, D, pairs):
+    """Geometry (N_pg, P, H, D) shared by every present INT8 (codes, scales) pair."""
+    shape = None
+    for codes, scales in pairs:
+        g = tuple(_int8_pool_geometry(codes, scales))
+        if g[2:] != (H, D):
+            raise ValueError(f"INT8 pool [N_pg, P, H, D] = {list(g)} does not hold rows of "
+                             f"H={H} heads x D={D}")
+        if shape is not None and g != shape:
+            raise ValueError(f"K and V pools differ in shape: {list(shape)} vs {list(g)}")
+        shape = g
+    if shape is None:
+        raise ValueError("no pool given")
+    return shape
+
+
 def cache_append(k, v, slot_mapping, k_cache, v_cache, *, stream=None):
     """Uncompressed paged write of 16-bit K/V rows (sawkv_cache_append)."""
     ref = k if k is not None else v
@@ -399,8 +448,12 @@ def cache_append(k, v, slot_mapping, k_cache, v_cache, *, stream=None):
             raise ValueError("caches must be contiguous [N_pg, P, H, D] of the K/V dtype")
         strides.append(x.stride(0))
     cache = k_cache if k is not None else v_cache
+    if k is not None and v is not None and tuple(k_cache.shape) != tuple(v_cache.shape):
+        raise ValueError("K and V caches differ in shape")
     if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T:
         raise ValueError("slot_mapping must be int64 [T]")
+    _on_gpu(k, v, slot_mapping, k_cache if k is not None else None,
+            v_cache if v is not None else None)
     _check(lib.sawkv_cache_append(_addr(k), _addr(v), strides[0], strides[1],
                                   _addr(slot_mapping), T, H, D,
                                   _addr(k_cache) if k is not None else None,
@@ -411,14 +464,12 @@ def cache_append(k, v, slot_mapping, k_cache, v_cache, *, stream=None):
 def int8_append(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, *, h=128, rot="none",
                 stream=None):
     """Token-wise INT8 append (sawkv_int8_append)."""
-    ref = k if k is not None else v
-    T, H, D, _ = _kv_geometry(ref)
-    ks_ = _kv_geometry(k)[3] if k is not None else 0
-    vs_ = _kv_geometry(v)[3] if v is not None else 0
-    pool = _int8_pool_geometry(k_codes, k_scales) if k is not None else \
-        _int8_pool_geometry(v_codes, v_scales)
+    T, H, D, ks_, vs_ = _kv_pair(k, v)
+    pairs = _present_pools(k, v, k_codes, v_codes, k_scales, v_scales)
+    pool = _int8_pools_for(H, D, pairs)
     if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T:
         raise ValueError("slot_mapping must be int64 [T]")
+    _on_gpu(k, v, slot_mapping, *[t for pair in pairs for t in pair])
     _check(lib.sawkv_int8_append(
         _addr(k), _addr(v), ks_, vs_, _addr(slot_mapping), T, H, D,
         _addr(k_codes) if k is not None else None, _addr(v_codes) if v is not None else None,
@@ -429,12 +480,16 @@ def int8_append(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, *, h=1
 def int8_gather(k_codes, v_codes, k_scales, v_scales, slot_mapping, *, h=128, rot="none",
                 k_out=None, v_out=None, want_k=True, want_v=True, stream=None):
     """INT8 read-back (sawkv_int8_gather). Returns (k_out, v_out)."""
-    pool = _int8_pool_geometry(k_codes, k_scales) if want_k else \
-        _int8_pool_geometry(v_codes, v_scales)
-    N_pg, P, H, D = pool
+    if not (want_k or want_v):
+        raise ValueError("neither K nor V wanted")
+    pairs = [pair for want, pair in ((want_k, (k_codes, k_scales)), (want_v, (v_codes, v_scales)))
+             if want]
+    H, D = _int8_pool_geometry(*pairs[0])[2:]
+    N_pg, P, H, D = _int8_pools_for(H, D, pairs)
     T = slot_mapping.numel()
-    if slot_mapping.dtype != torch.int64:
+    if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1:
         raise ValueError("slot_mapping must be int64 [T]")
+    _on_gpu(slot_mapping, k_out, v_out, *[t for pair in pairs for t in pair])
     dev = (k_codes if want_k else v_codes).device
     if want_k and k_out is None:
         k_out = torch.empty((T, H, D), dtype=torch.float16, device=dev)
@@ -442,6 +497,11 @@ def int8_gather(k_codes, v_codes, k_scales, v_scales, slot_mapping, *, h=128, ro
         v_out = torch.empty((T, H, D), dtype=torch.float16, device=dev)
     k_out = k_out if want_k else None
     v_out = v_out if want_v else None
+    for o in (k_out, v_out):
+        if o is not None and (o.dtype != torch.float16 or tuple(o.shape) != (T, H, D)
+                              or not o.is_contiguous()):
+            raise ValueError("outputs must be contiguous fp16 [T, H, D]")
+    _on_gpu(k_out, v_out)
     _check(lib.sawkv_int8_gather(
         _addr(k_codes) if want_k else None, _addr(v_codes) if want_v else None,
         _addr(k_scales) if want_k else None, _addr(v_scales) if want_v else None,

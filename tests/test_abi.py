@@ -359,3 +359,22 @@ def test_control_specific_validation(lib):
                slots=None) == OK
     assert ctl(lib, "gather8", T=0, ko=None, vo=None, kc=None, vc=None, kss=None, vss=None,
                slots=None) == OK
+
+
+@pytest.mark.parametrize("stride", [-8, -1024, -(1 << 40), 0, 8])
+@pytest.mark.parametrize("which", ["k", "v"])
+def test_input_stride_below_row_is_rejected_by_every_append(lib, stride, which):
+    """A K or V token stride below H*D (negative included) is refused before
+    any launch by every entry point that reads fp16 K/V rows."""
+    kw = {"ks": stride} if which == "k" else {"vs": stride}
+    assert app(lib, **kw) == EINVAL
+    assert b"stride" in lib.sawkv_last_error()
+    ks, vs = kw.get("ks", 1024), kw.get("vs", 1024)
+    assert lib.sawkv_naive_int4_append(K, V, ks, vs, S, 64, 8, 128, KC, VC, KS, VS, 16, 16,
+                                       None) == EINVAL
+    arr = (LayerDesc * 2)(good_layer(0), good_layer(1))
+    assert lib.sawkv_quantize_append_layers(arr, 2, ks, vs, S, 256, 8, 128, 64, 16, 128, 1,
+                                            None) == EINVAL
+    assert ctl(lib, "append8", **kw) == EINVAL
+    assert ctl(lib, "cache", **kw) == EINVAL
+    assert b"stride" in lib.sawkv_last_error()
