@@ -181,9 +181,9 @@ def test_no_flush_to_zero():
 # scale, codes, packing: worked cases
 # --------------------------------------------------------------------------
 
-def _load_golden():
+def _load_golden(name="closed_forms.txt"):
     cases = []
-    with open(os.path.join(GOLDEN, "closed_forms.txt")) as f:
+    with open(os.path.join(GOLDEN, name)) as f:
         cur = {}
         for line in f:
             line = line.strip()
@@ -480,6 +480,84 @@ def test_gather_reconstruction_bound():
         bound = 0.5 * s16.astype(np.float64) * np.sqrt(128) * (1 + 1e-3) \
             + 2.0 ** -11 * np.linalg.norm(x.astype(np.float64), axis=-1) * 2
         assert np.all(err <= bound)
+
+
+def _pack_by_hand(q):
+    """Two's-complement nibbles, element 2k in the low nibble of byte k."""
+    return np.array([(q[2 * k] & 15) | ((q[2 * k + 1] & 15) << 4) for k in range(len(q) // 2)],
+                    np.uint8)
+
+
+def _f32_staged_fwht(y, h):
+    """F_h by butterfly stages (strides 1, 2, ..., h/2), every sum rounded to
+    float32 with exact rational arithmetic: used only to show that a case
+    tells the scale-first order apart."""
+    y = [rn(Fraction(v)) for v in y]
+    s = 1
+    while s < h:
+        for i in range(len(y)):
+            if i % (2 * s) < s:
+                a, b = y[i], y[i + s]
+                y[i], y[i + s] = rn(a + b), rn(a - b)
+        s *= 2
+    return y
+
+
+@pytest.mark.parametrize("case", _load_golden("read_back.txt"), ids=lambda c: c["case"])
+def test_golden_read_back_rounding_order(case):
+    """decode_vectors = f16(f32(c_h * F_h(q * s))) on every channel, with the
+    exact value from the explicit Sylvester matrix and rational arithmetic.
+    The case holds a channel where f32(c_h * s * F) is an fp16 midpoint, so
+    rounding once straight to fp16, or applying c_h before the butterflies,
+    gives other bits (checked here too)."""
+    h = int(case["h"])
+    q = [int(t) for t in case["codes"].split()]
+    assert len(q) == 128
+    s_bits = int(case["scale_bits"], 16)
+    s16 = np.array([s_bits], np.uint16).view(np.float16)
+    s = Fraction(float(s16[0]))
+    out = O.decode_vectors(_pack_by_hand(q)[None], s16, h, True)[0]
+
+    Hm = np.kron(np.eye(128 // h, dtype=np.int64), scipy.linalg.hadamard(h).astype(np.int64))
+    F = Hm @ np.array(q, np.int64)
+    c = Fraction(float(O.c_h(h)))
+    want = [f16_bits(float(rn(rn(c * s * int(f)), F16))) for f in F]
+    assert [f16_bits(float(v)) for v in out] == want
+
+    e = int(case["elem"])
+    assert int(F[e]) == int(case["F"])
+    assert f32_bits(float(rn(c * s * int(F[e])))) == int(case["f32_bits"], 16)
+    assert want[e] == int(case["want_bits"], 16)
+    other = int(case["other_bits"], 16)
+    assert f16_bits(float(rn(c * s * int(F[e]), F16))) == other          # one rounding
+    scaled_first = _f32_staged_fwht([rn(c * rn(qi * s)) for qi in q], h)
+    assert f16_bits(float(rn(scaled_first[e], F16))) == other            # c_h first
+
+
+def test_mse_closed_form():
+    """mse(x_hat, x) = sum of squared differences / number of elements, in
+    float64: x on a 2^-4 grid, x_hat = x + k * 2^-8 (both exact in fp16), so
+    the exact value is sum(k^2) * 2^-16 / N; every partial sum is a multiple
+    of 2^-16 below 2^15, so float64 accumulation is exact and the oracle must
+    return this value exactly."""
+    rng = np.random.default_rng(31)
+    shape = (64, 4, 128)
+    N = int(np.prod(shape))
+    x = (rng.integers(-64, 64, size=shape) * 2.0 ** -4).astype(np.float16)
+    k = rng.integers(-255, 256, size=shape)
+    k[rng.random(shape) < 0.3] = 0
+    x_hat = (x.astype(np.float64) + k * 2.0 ** -8).astype(np.float16)
+    assert np.array_equal(x_hat.astype(np.float64) - x.astype(np.float64), k * 2.0 ** -8)
+    exact = Fraction(int(np.sum(k.astype(np.int64) ** 2)), 2 ** 16 * N)
+    got = O.mse(x_hat, x)
+    assert Fraction(got) == exact
+    # the case tells apart a mean of |d| and a float16 accumulation
+    assert Fraction(float(np.mean(np.abs(k * 2.0 ** -8)))) != exact
+    d16 = x_hat - x
+    assert Fraction(float(np.sum(d16 * d16, dtype=np.float16)) / N) != exact
+    # and the sum over a whole tensor, not a mean over rows of their sums
+    assert O.mse(x_hat[:1], x[:1]) == float(
+        Fraction(int(np.sum(k[:1].astype(np.int64) ** 2)), 2 ** 16 * (N // 64)))
 
 
 # --------------------------------------------------------------------------
