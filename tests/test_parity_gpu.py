@@ -2,12 +2,16 @@
 
 Codes and scales must match the oracle byte for byte; gathered fp16 rows must
 match the oracle's read-back byte for byte and, per vector, within 1e-3 of the
-vector's largest magnitude (the tolerance asked of the read path). Small and
-ragged cases compare every byte of the pools; the full-size workloads compare
-seeded samples of tokens element by element, plus pool-wide properties that
-hold at any size (exactly the mapped rows are written).
+vector's largest magnitude (the tolerance asked of the read path). Every case,
+the full-size prefill, sweep and long workloads included, compares every byte
+of the pools (sentinel bytes outside the mapped rows included) and every
+gathered row; the oracle runs in-process on token chunks in a thread pool (no
+worker process is forked once this process has touched the GPU). The decode
+workload compares every appended row of each of its 36 layers and, for the
+first and the last layer, that no other row changed.
 """
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -364,7 +368,7 @@ def test_division_route_exhaustive_fp16(env):
 
 
 # --------------------------------------------------------------------------
-# full-size workloads: sampled tokens + pool-wide properties
+# full-size workloads: every byte of the pools, every gathered row
 # --------------------------------------------------------------------------
 
 def check_written_rows(env, gp, slots, n_slots, H):
@@ -380,8 +384,8 @@ def check_written_rows(env, gp, slots, n_slots, H):
         assert bool((untouched == SENT_CODE).all())
 
 
-def compare_sampled(env, gp, k, v, slots, sample, h, rot, what):
-    """Pool rows of sampled tokens vs the oracle's encoding of those tokens."""
+def compare_rows(env, gp, k, v, slots, sample, h, rot, what):
+    """Pool rows of the given tokens vs the oracle's encoding of those tokens."""
     torch, S = env
     H = k.shape[1]
     idx = torch.from_numpy(slots[sample]).cuda()
@@ -407,14 +411,49 @@ def test_decode_workload_36_layers(env):
         S.quantize_append(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), sd, *gp,
                           h=wl.h, rot=ROTS[wl.rot_mode])
         torch.cuda.synchronize()
-        compare_sampled(env, gp, k, v, slots, np.arange(wl.T), wl.h, wl.rot_mode,
+        compare_rows(env, gp, k, v, slots, np.arange(wl.T), wl.h, wl.rot_mode,
                         f"decode layer {layer}")
         if layer in (0, wl.layers - 1):
             check_written_rows(env, gp, slots, wl.n_slots, wl.H)
         del gp
 
 
-def _full(env, name, h=None, rot=None, n_sample=4096, gather=False):
+ORACLE_CHUNK = 8192          # tokens per oracle task
+
+
+def oracle_pools_threaded(k, v, slots, n_pg, P, h, rot):
+    """The oracle's pools for the whole batch, encoded in token chunks by a
+    thread pool; chunks write disjoint slots of the same sentinel pools."""
+    T, H, D = k.shape
+    want = np_pools(n_pg, P, H, D)
+
+    def enc(a):
+        b = min(T, a + ORACLE_CHUNK)
+        O.quantize_append(k[a:b], v[a:b], slots[a:b], *want, h=h, rot_mode=rot)
+
+    with ThreadPoolExecutor(W._workers()) as ex:
+        list(ex.map(enc, range(0, T, ORACLE_CHUNK)))
+    return want
+
+
+def compare_gather_threaded(want, slots, h, rot, ko, vo, what):
+    """Every gathered row of K and V against the oracle's read-back of the
+    oracle's pools, chunk by chunk in a thread pool."""
+    T = len(slots)
+
+    def cmp(a):
+        b = min(T, a + ORACLE_CHUNK)
+        rk, rv = O.dequant_gather(*want, slots[a:b], h=h, rot_mode=rot)
+        assert_rows_close(ko[a:b], rk, f"{what} k gather tokens {a}:{b}")
+        assert_rows_close(vo[a:b], rv, f"{what} v gather tokens {a}:{b}")
+
+    with ThreadPoolExecutor(W._workers()) as ex:
+        list(ex.map(cmp, range(0, T, ORACLE_CHUNK)))
+
+
+def _full(env, name, h=None, rot=None, gather=True):
+    """A full-size workload: the whole pool byte for byte and every gathered
+    row against the oracle."""
     torch, S = env
     wl = W.WORKLOADS[name]
     h = wl.h if h is None else h
@@ -427,33 +466,34 @@ def _full(env, name, h=None, rot=None, n_sample=4096, gather=False):
     say(f"{name}: append h={h} rot={ROTS[rot]}")
     S.quantize_append(kd, vd, sd, *gp, h=h, rot=ROTS[rot])
     torch.cuda.synchronize()
-    rng = np.random.default_rng(wl.wid * 7 + h + rot)
-    sample = np.sort(rng.choice(wl.T, size=min(n_sample, wl.T), replace=False))
-    sample[0], sample[-1] = 0, wl.T - 1
-    compare_sampled(env, gp, k, v, slots, sample, h, rot, f"{name} h={h} rot={rot}")
-    check_written_rows(env, gp, slots, wl.n_slots, wl.H)
+    del kd, vd
+    got = [to_np(x) for x in gp]
+    say(f"{name}: oracle on {wl.T} tokens, {W._workers()} threads")
+    want = oracle_pools_threaded(k, v, slots, wl.N_pg, wl.P, h, rot)
+    assert_pools_equal(got, want, f"{name} h={h} rot={rot}")
+    del got
     if gather:
-        say(f"{name}: gather")
+        say(f"{name}: gather of {wl.T} tokens")
         ko, vo = S.dequant_gather(*gp, sd, h=h, rot=ROTS[rot])
         torch.cuda.synchronize()
-        for x, out, rotated in ((k, ko, rot != O.ROT_NONE), (v, vo, rot == O.ROT_KV)):
-            want = O.decode_vectors(*O.encode_vectors(x[sample], h, rotated), h, rotated)
-            got = to_np(out[torch.from_numpy(sample).cuda()])
-            assert_rows_close(got, want, f"{name} gather")
+        del gp
+        ko, vo = to_np(ko), to_np(vo)
+        compare_gather_threaded(want, slots, h, rot, ko, vo, f"{name} h={h} rot={rot}")
+    say(f"{name}: done")
     return wl
 
 
 def test_prefill_workload(env):
-    _full(env, "prefill", gather=True)
+    _full(env, "prefill")
 
 
 @pytest.mark.parametrize("h,rot", W.SWEEP_VARIANTS)
 def test_sweep_workload(env, h, rot):
-    _full(env, "sweep", h=h, rot=rot, n_sample=2048, gather=True)
+    _full(env, "sweep", h=h, rot=rot)
 
 
 def test_long_workload_round_trip(env):
-    wl = _full(env, "long", n_sample=2048, gather=True)
+    wl = _full(env, "long")
     assert wl.T == wl.n_slots          # exact-fit pool: every slot written
 
 
