@@ -1,21 +1,31 @@
 """Benchmark of the fused Hadamard + INT4 paged append (sawkv) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long]
     python bench.py --workload attn     (decode attention over the INT4 pool)
     python bench.py --workload attn_long  (the same over 64 contexts of 32768 tokens)
     python bench.py --workload concurrency  (rotated vs naive INT4 across 1..256
                                              concurrent decodes)
     python bench.py --heads 1   (one GPU's share of the 8 KV heads under TP-8)
 
+The default workload is the long-context batch: 64 sequences x 32768 tokens,
+8 KV heads x 128, page 32 in a shuffled pool, K and V rotated with h = 128.
 One step = one sawkv_quantize_append call over the workload's batch (rotate,
 token-wise INT4, pack, scatter into the paged pool: the whole write path).
-Inputs are generated, uploaded and resident in HBM before timing starts.
+Inputs are generated, uploaded and resident in HBM before timing starts;
+after the warm-up steps, launches of the same step run for at least 100 ms
+(reported under "settle") so that the timed steps start at steady clocks.
 Prints ONE JSON line. Alongside the step it times, on the same batch:
   * the naive-INT4 control (sawkv_naive_int4_append), interleaved with the
-    rotated kernel, for the rotate-vs-naive ratio;
+    rotated kernel over 9 rounds, for the rotate-vs-naive ratio and its
+    bootstrap 95 % interval;
   * the same two kernels with cold caches (an untimed 1 GiB read before every
     timed launch);
-  * the read-back (sawkv_dequant_gather) of the same slots;
+  * the read-back (sawkv_dequant_gather) of the same slots, back to back and
+    cold;
+  * the append's access-pattern control (sawkv_append_pattern_control: the
+    same loads and stores, no arithmetic), writing to the mapped slots and to
+    token order, interleaved with the append: the bandwidth the append's
+    pattern reaches at all on this device;
   * (prefill, sweep) the uncompressed fp16 cache write and token-wise INT8
     append / read-back, with INT8's reconstruction error;
   * the CPU oracle on a bounded sample of the same batch (a baseline only).
@@ -164,6 +174,7 @@ def cpu_baseline(wl, h, rot, sample_tokens):
     _FORK_SHARED.clear()
     return {"value": round(bytes_sample / dt_n / 1e9, 4), "unit": "GB/s", "cores": n_proc,
             "kind": "oracle", "tokens_per_s": round(sample_tokens / dt_n, 1),
+            "sample_tokens": sample_tokens,
             "seconds": round(dt_n, 3),
             "sample": f"first {sample_tokens} tokens of the {wl.name} batch (K and V), numpy "
                       f"float32 oracle, {n_proc} forked processes on contiguous token chunks "
@@ -173,6 +184,94 @@ def cpu_baseline(wl, h, rot, sample_tokens):
                                "seconds": round(dt_1, 2)},
             "pools_equal_across_legs": same,
             "cpu_model": _cpu_model(), "numpy": np.__version__}
+
+LLC_BYTES = 256 * 1024 * 1024    # MI355X last-level (Infinity) cache
+
+
+def settle_clocks(torch, fn, min_ms=100.0):
+    """Launch `fn` until at least `min_ms` of wall time has passed (synchronised),
+    so that the timed steps that follow start at steady clocks."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(8):
+            fn()
+        n += 8
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3
+        if ms >= min_ms:
+            return {"launches": n, "ms": round(ms, 1), "min_ms": min_ms}
+
+
+def bootstrap_ratio_ci(a, b, n=2000, seed=0):
+    """95 % bootstrap interval of median(a) / median(b)."""
+    rng = np.random.default_rng(seed)
+    boots = [np.median(rng.choice(a, len(a))) / np.median(rng.choice(b, len(b)))
+             for _ in range(n)]
+    return [round(float(np.percentile(boots, 2.5)), 4), round(float(np.percentile(boots, 97.5)), 4)]
+
+
+def pct(a):
+    """p5 / median / p95 of a list of ms, in us."""
+    return {q: round(float(np.percentile(a, v)) * 1e3, 2)
+            for q, v in (("p5", 5), ("median", 50), ("p95", 95))}
+
+
+class Flush:
+    """An untimed 1 GiB device read before each timed launch (more than the
+    256 MB last-level cache plus L2; a read leaves only clean lines)."""
+
+    def __init__(self, torch, dev):
+        self.torch = torch
+        self.buf = torch.ones(256 * 1024 * 1024, dtype=torch.int32, device=dev)
+        self.sum = torch.empty((1,), dtype=torch.int64, device=dev)
+
+    def cold(self, fns, n, stream):
+        torch = self.torch
+        res = {name: [] for name in fns}
+        for _ in range(n):
+            for name, fn in fns.items():
+                torch.sum(self.buf, dim=(0,), dtype=torch.int64, out=self.sum[0])
+                c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                c0.record(stream)
+                fn()
+                c1.record(stream)
+                torch.cuda.synchronize()
+                res[name].append(c0.elapsed_time(c1))
+        return res
+
+
+def pattern_ceiling(S, torch, wl, kv, slots, pools, step_rot, timed, bytes_step, n_ab):
+    """The append's loads and stores with no arithmetic (the access-pattern
+    control), at the workload's slots and in token order, interleaved with
+    the rotated append over 5 rounds on the same inputs and pools."""
+    k, v = kv
+    fns = {"same_pattern": S.PatternControlCall(k, v, slots, *pools, placement="slots"),
+           "token_order": S.PatternControlCall(k, v, slots, *pools, placement="token_order"),
+           "append": step_rot}
+    for fn in fns.values():
+        for _ in range(5):
+            fn()
+    ms = {name: [] for name in fns}
+    for _ in range(5):
+        for name, fn in fns.items():
+            ms[name].append(timed(fn, n_ab))
+    med = {name: float(np.median(v_)) for name, v_ in ms.items()}
+    gb = {name: bytes_step / (m * 1e-3) / 1e9 for name, m in med.items()}
+    step_rot()                      # leave the pools holding the append's codes
+    torch.cuda.synchronize()
+    return {"same_pattern_GBps": round(gb["same_pattern"], 1),
+            "token_order_GBps": round(gb["token_order"], 1),
+            "append_GBps_interleaved": round(gb["append"], 1),
+            "append_over_same_pattern": round(gb["append"] / gb["same_pattern"], 4),
+            "same_pattern_us": round(med["same_pattern"] * 1e3, 2),
+            "token_order_us": round(med["token_order"] * 1e3, 2),
+            "append_us": round(med["append"] * 1e3, 2),
+            "rounds": 5, "steps_per_round": n_ab,
+            "note": ("sawkv_append_pattern_control: the append's grid, loads and stores with "
+                     "none of the method's arithmetic; same_pattern writes the mapped slots, "
+                     "token_order writes row t*H + head (contiguous pages)")}
 
 
 def mse_gpu(torch, out, ref):
@@ -338,8 +437,9 @@ def bench_attention(args):
 
     for _ in range(args.warmup):
         call()
-    torch.cuda.synchronize()
+    settle = settle_clocks(torch, call)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
     for _ in range(args.steps):
@@ -352,12 +452,13 @@ def bench_attention(args):
     gbps = nbytes / (wall_ms * 1e-3) / 1e9
     achieved = nbytes / (event_ms * 1e-3) / 1e9
 
-    rounds, n_ab = 7, max(20, args.steps // 4)
+    rounds, n_ab = 9, max(20, args.steps // 4)
     rot_ms, naive_ms = [], []
     for _ in range(rounds):
         naive_ms.append(timed(naive, n_ab))
         rot_ms.append(timed(call, n_ab))
     ratio = float(np.median(rot_ms) / np.median(naive_ms))
+    ratio_ci = bootstrap_ratio_ci(rot_ms, naive_ms)
 
     # other query-head groupings on the same pool (fresh queries): 8 per KV
     # head (64 query heads, as Llama-2-70B) and 1 (multi-head attention)
@@ -416,8 +517,9 @@ def bench_attention(args):
                                "attn_combine_kernel)"},
         "vs_naive": {"rot_ms_median": round(float(np.median(rot_ms)), 5),
                      "naive_ms_median": round(float(np.median(naive_ms)), 5),
-                     "rot_over_naive": round(ratio, 4), "rounds": rounds,
-                     "steps_per_round": n_ab},
+                     "rot_over_naive": round(ratio, 4), "rot_over_naive_ci95": ratio_ci,
+                     "rounds": rounds, "steps_per_round": n_ab},
+        "settle": settle,
         "other_head_groupings": groupings,
         "workspace_bytes": int(call.workspace.numel()),
         "kernel_source_hash": kernel_source_hash(ATTN_SRC),
@@ -533,7 +635,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="prefill",
+    ap.add_argument("--workload", default="long",
                     choices=["prefill", "decode", "sweep", "long", "attn", "attn_long",
                              "concurrency"])
     ap.add_argument("--h", type=int, default=None)
@@ -601,15 +703,9 @@ def main():
         step_rot = S.LayersCall(kvs, slots, pools, h=h, rot=ROT_NAME[rot])
         step_naive = S.LayersCall(kvs, slots, naive_pools, h=h, rot="none")
     else:
-        step_rot = per_layer_rot
-
-        def step_naive():
-            S.naive_int4_append(kvs[0][0], kvs[0][1], slots, *naive_pools[0])
-
-    def step_gather(outs):
-        for layer in range(layers):
-            S.dequant_gather(*pools[layer], slots, h=h, rot=ROT_NAME[rot],
-                             k_out=outs[layer][0], v_out=outs[layer][1])
+        # arguments checked and marshalled once; each call only launches
+        step_rot = S.AppendCall(kvs[0][0], kvs[0][1], slots, *pools[0], h=h, rot=ROT_NAME[rot])
+        step_naive = S.NaiveAppendCall(kvs[0][0], kvs[0][1], slots, *naive_pools[0])
 
     def timed(fn, n):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -621,11 +717,19 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n      # ms per step
 
-    # warm-up, then the timed K steps (wall clock bracketed by synchronize)
+    tokens = wl.T                      # new tokens per step (each appended to every layer)
+    bytes_step = wl.T * wl.bytes_per_token() * layers
+    read_bytes = wl.T * (wl.H * 2 * wl.D * 2 + 8) * layers       # fp16 K, V and slots
+
+    # warm-up, clock settle, then the timed K steps (wall clock bracketed by
+    # synchronize; events on the launch stream)
     for _ in range(args.warmup):
         step_rot()
-    torch.cuda.synchronize()
+    settle = settle_clocks(torch, step_rot)
+    print(f"[bench] settle: {settle['launches']} launches in {settle['ms']} ms; timing "
+          f"{args.steps} steps", file=sys.stderr, flush=True)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
     for _ in range(args.steps):
@@ -634,61 +738,56 @@ def main():
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     event_ms = e0.elapsed_time(e1) / args.steps
-
-    tokens = wl.T                      # new tokens per step (each appended to every layer)
-    bytes_step = wl.T * wl.bytes_per_token() * layers
     gbps = bytes_step / (wall_ms * 1e-3) / 1e9
     achieved = bytes_step / (event_ms * 1e-3) / 1e9
 
     # rotated vs naive: interleaved rounds on the same inputs and pools
-    rounds = 7
+    rounds = 9
     n_ab = max(20, args.steps // 4)
     rot_ms, naive_ms = [], []
     for _ in range(rounds):
         naive_ms.append(timed(step_naive, n_ab))
         rot_ms.append(timed(step_rot, n_ab))
     ratio = float(np.median(rot_ms) / np.median(naive_ms))
-    rng = np.random.default_rng(0)
-    boots = []
-    for _ in range(2000):
-        a = rng.choice(rot_ms, len(rot_ms))
-        b = rng.choice(naive_ms, len(naive_ms))
-        boots.append(np.median(a) / np.median(b))
-    ratio_ci = [round(float(np.percentile(boots, 2.5)), 4), round(float(np.percentile(boots, 97.5)), 4)]
+    ratio_ci = bootstrap_ratio_ci(rot_ms, naive_ms)
+    print(f"[bench] rot/naive {ratio:.4f} {ratio_ci}", file=sys.stderr, flush=True)
 
     # cold caches: every timed launch follows an untimed read of 1 GiB (larger
     # than the 256 MB last-level cache plus L2), which leaves only clean lines
     # behind (a fill would leave dirty ones, whose write-back lands in the timed
     # launch); rotated and naive interleaved
-    flush = torch.ones(256 * 1024 * 1024, dtype=torch.int32, device=dev)
-    fsum = torch.empty((1,), dtype=torch.int64, device=dev)
+    flush = Flush(torch, dev)
     n_cold = 30 if wl.T * layers <= 262144 else 10
-    cold = {"rot": [], "naive": []}
-    for _ in range(n_cold):
-        for name, fn in (("naive", step_naive), ("rot", step_rot)):
-            torch.sum(flush, dim=(0,), dtype=torch.int64, out=fsum[0])
-            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            c0.record(stream)
-            fn()
-            c1.record(stream)
-            torch.cuda.synchronize()
-            cold[name].append(c0.elapsed_time(c1))
-    del flush, fsum
-
-    def pct(a):
-        return {q: round(float(np.percentile(a, v)) * 1e3, 2)
-                for q, v in (("p5", 5), ("median", 50), ("p95", 95))}
+    cold = flush.cold({"naive": step_naive, "rot": step_rot}, n_cold, stream)
     cold_out = {"rot_us": pct(cold["rot"]), "naive_us": pct(cold["naive"]),
                 "rot_over_naive": round(float(np.median(cold["rot"]) / np.median(cold["naive"])), 4),
                 "GBps_rot_median": round(bytes_step / (np.median(cold["rot"]) * 1e-3) / 1e9, 1),
                 "launches": n_cold,
                 "flush": "1 GiB device read before every timed launch (not timed)"}
 
-    # read-back of the same slots
+    # read-back of the same slots: back to back, then cold
     outs = [(torch.empty_like(kvs[l][0]), torch.empty_like(kvs[l][1])) for l in range(layers)]
+    gcalls = [S.GatherCall(*pools[l], slots, outs[l][0], outs[l][1], h=h, rot=ROT_NAME[rot])
+              for l in range(layers)]
+
+    def gather_fn():
+        for c in gcalls:
+            c()
     for _ in range(3):
-        step_gather(outs)
-    g_ms = timed(lambda: step_gather(outs), max(20, args.steps // 2))
+        gather_fn()
+    g_ms = timed(gather_fn, max(20, args.steps // 2))
+    g_cold = flush.cold({"gather": gather_fn}, n_cold, stream)["gather"]
+    g_read = wl.T * (wl.H * 2 * (wl.D // 2 + 2) + 8) * layers       # codes, scales, slots
+    print(f"[bench] gather {g_ms * 1e3:.1f} us back to back, {np.median(g_cold) * 1e3:.1f} us "
+          f"cold", file=sys.stderr, flush=True)
+
+    # the append's own access pattern with no arithmetic, interleaved with the
+    # append: at the workload's slots and in token order
+    attainable = {}
+    if layers == 1:
+        attainable = pattern_ceiling(S, torch, wl, kvs[0], slots, pools[0], step_rot, timed,
+                                     bytes_step, n_ab)
+    del flush
 
     extra = {}
     if args.workload == "sweep":
@@ -707,17 +806,20 @@ def main():
         extra["mse"] = {"k": mse_gpu(torch, ko, kvs[0][0]), "v": mse_gpu(torch, vo, kvs[0][1])}
     if args.workload in ("prefill", "sweep"):
         extra["controls"] = controls(S, torch, wl, kvs[0], slots, timed, stream, h, rot)
+    del outs, gcalls
 
     # attainable-bandwidth context on this machine: a 256 MiB device copy (torch)
     cbuf = torch.empty(64 * 1024 * 1024, dtype=torch.int32, device=dev)
     cdst = torch.empty_like(cbuf)
     cdst.copy_(cbuf)
     c_ms = timed(lambda: cdst.copy_(cbuf), 50)
-    copy_gbps = 2 * cbuf.numel() * 4 / (c_ms * 1e-3) / 1e9
+    attainable["copy_256MiB_GBps"] = round(2 * cbuf.numel() * 4 / (c_ms * 1e-3) / 1e9, 1)
+    attainable["copy_note"] = "torch device-to-device copy on the same GPU, context only"
     del cbuf, cdst
 
     # the committed counters cover the workloads at their own shapes only
     traffic = measured_traffic(args.workload) if not args.heads else None
+    resident = read_bytes <= LLC_BYTES
     out = {
         "metric": METRIC,
         "value": round(gbps, 2),
@@ -735,19 +837,26 @@ def main():
                    "layers_appended_per_token": layers,
                    "heads": wl.H, "head_dim": wl.D, "block_size_h": h,
                    "rotation": ROT_NAME[rot], "page_size": wl.P, "pages": wl.N_pg,
-                   "layers_per_step": layers, "parallelism": "single GPU"},
+                   "layers_per_step": layers, "parallelism": "single GPU",
+                   "cpu_sample_tokens": None if cpu is None else cpu["sample_tokens"]},
         "step": ("sawkv_quantize_append_layers: every layer of the decode step in one launch"
                  if layers > 1 else
                  "sawkv_quantize_append over the batch (rotate, token-wise INT4, pack, "
                  "paged scatter)"),
         "tokens_per_s": round(tokens / (wall_ms * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "cache_resident": resident,
+        "settle": settle,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": bytes_step,
+                     "event_us_per_launch": round(event_ms * 1e3, 2),
                      "kernel": ("sawkv::append_layers_kernel" if layers > 1
-                                else "sawkv::append_kernel")},
+                                else "sawkv::append_kernel"),
+                     **({"frac_of_same_pattern":
+                         round(achieved / attainable["same_pattern_GBps"], 4)}
+                        if "same_pattern_GBps" in attainable else {})},
         "vs_naive": {"rot_ms_median": round(float(np.median(rot_ms)), 5),
                      "naive_ms_median": round(float(np.median(naive_ms)), 5),
                      "rot_over_naive": round(ratio, 4),
@@ -756,10 +865,14 @@ def main():
                      "rounds": rounds, "steps_per_round": n_ab},
         "gather": {"ms_per_step": round(g_ms, 5),
                    "GBps": round(bytes_step / (g_ms * 1e-3) / 1e9, 2),
-                   "tokens_per_s": round(tokens / (g_ms * 1e-3), 1)},
+                   "tokens_per_s": round(tokens / (g_ms * 1e-3), 1),
+                   "cache_resident": g_read <= LLC_BYTES,
+                   "cold": {"us": pct(g_cold),
+                            "GBps_median": round(bytes_step / (np.median(g_cold) * 1e-3) / 1e9, 1),
+                            "launches": n_cold,
+                            "flush": "1 GiB device read before every timed launch (not timed)"}},
         "cold": cold_out,
-        "attainable": {"copy_256MiB_GBps": round(copy_gbps, 1),
-                       "note": "torch device-to-device copy on the same GPU, context only"},
+        "attainable": attainable,
         "kernel_source_hash": kernel_source_hash(),
         **extra,
     }

@@ -227,6 +227,43 @@ int sawkv_int8_gather(const void* k_codes, const void* v_codes,
                       void* stream);
 
 /*
+ * Access-pattern control of the INT4 append (a measurement control, not part
+ * of the method). The pages place the fused append in a data flow bounded by
+ * memory bandwidth, with the rotation's arithmetic hidden inside it
+ * (gist.science summary, §2 Metodologia, BDR item 3); this call moves the
+ * same bytes along the same paths with none of that arithmetic, so its time
+ * is what the append's access pattern can reach at all on the device.
+ *
+ * It runs the append's grid and issues the append's loads (every fp16 row of
+ * K and V, 16 bytes per lane, and the slot of every token) and writes, per
+ * (token t, head j) vector, a 64-byte row and a 2-byte value:
+ *   row word c (c = 0..15, little-endian uint32) = xor of the four uint32
+ *       words of the input row's 16-byte piece c
+ *   value bits = (word 0) xor (word 0 >> 16), low 16 bits
+ * to the codes and scales pools at
+ *   placement SAWKV_PLACE_SLOTS:       the row the append writes (slot*H + j;
+ *                                      slots < 0 or >= N_pg*P are skipped)
+ *   placement SAWKV_PLACE_TOKEN_ORDER: row t*H + j (needs T <= N_pg*P), i.e.
+ *                                      the same writes to contiguous pages
+ * Arguments, validation and sizes as sawkv_naive_int4_append; placement
+ * outside the two values, or T > N_pg*P in token order, is SAWKV_EINVAL.
+ */
+enum {
+  SAWKV_PLACE_SLOTS = 0,
+  SAWKV_PLACE_TOKEN_ORDER = 1
+};
+
+int sawkv_append_pattern_control(const void* k, const void* v,
+                                 int64_t k_stride, int64_t v_stride,
+                                 const int64_t* slot_mapping, int64_t T,
+                                 int32_t H, int32_t D,
+                                 void* k_codes, void* v_codes,
+                                 void* k_scales, void* v_scales,
+                                 int64_t N_pg, int32_t P,
+                                 int32_t placement,
+                                 void* stream);
+
+/*
  * Decode attention over the paged INT4 pools: one new query token per
  * sequence attends to every cached token of its sequence. This is the consumer
  * the pages fuse dequantisation into (ainews.cool, "技术深度解析" item 3:

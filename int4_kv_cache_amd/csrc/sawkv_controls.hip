@@ -1,5 +1,8 @@
 // sawkv controls (gfx950): the uncompressed paged cache write and token-wise
-// INT8, the baselines the INT4 cache is compared against (gist.science
+// INT8, the baselines the INT4 cache is compared against, and an
+// access-pattern control of the INT4 append (its loads and stores with no
+// arithmetic of the method) that measures the bandwidth the append's pattern
+// can reach at all (gist.science
 // summary of SAW-INT4, §4 Risultati Sperimentali: accuracy and system
 // throughput against a BF16 cache; ainews.cool, the comparison table under
 // "技术深度解析": a uniform INT8 cache).
@@ -227,6 +230,52 @@ __global__ __launch_bounds__(kThreads) void cache_append_kernel(CacheParams p) {
   C.cache[(slot * p.H + head) * 16 + piece] = C.src[t * C.stride16 + head * 16 + piece];
 }
 
+// ---- access-pattern control of the INT4 append ----
+//
+// The INT4 append's grid, loads and stores with none of the method's
+// arithmetic: each wave fetches its 16 vectors exactly as the append does
+// (fetch_batch: the same 16-byte loads of the fp16 rows and the same slot
+// load), folds each 16-byte input piece into one 32-bit word by xor, and
+// stores the 64-byte row and the 2-byte scale where the append would store
+// the codes and the scale. With kTokenOrder the rows go to row t*H + head
+// (token order) instead of the mapped slot, which shows what the same loads
+// reach when the destination pages are contiguous.
+template <bool kTokenOrder>
+__device__ __forceinline__ void pattern_tensor(const AppendTensor& A, const AppendParams& p) {
+  const int lane = threadIdx.x & 63;
+  const int lam = lane & 3;
+  const int vq = lane >> 2;
+  const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  WavePos w;
+  w.v0 = (blockIdx.x * kWaves + wave) * kVecPerWave;
+  if (w.v0 >= (uint32_t)p.TH) return;
+  w.t0 = w.v0 / (uint32_t)p.H;
+  w.h0 = w.v0 - w.t0 * (uint32_t)p.H;
+  const Fetched f = fetch_batch(A, p, w, lam, vq);
+  uint32_t d[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[i] = f.raw[i].x ^ f.raw[i].y ^ f.raw[i].z ^ f.raw[i].w;
+  const uint16_t sbits = (uint16_t)(d[0] ^ (d[0] >> 16));
+  int64_t row;
+  if constexpr (kTokenOrder) {
+    row = (int64_t)w.v0 + vq;                  // t * H + head
+    if (!f.in_range) return;
+  } else {
+    if (!(f.in_range && f.slot >= 0 && f.slot < p.n_slots)) return;
+    row = f.slot * p.H + f.head;
+  }
+  uint8_t* dst = A.codes + row * (kD / 2) + 4 * lam;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(dst + 16 * i) = d[i];
+  if (lam == 0) A.scales[row] = __builtin_bit_cast(__half, sbits);
+}
+
+template <bool kTokenOrder>
+__global__ __launch_bounds__(kThreads) void pattern_kernel(AppendParams p) {
+  if (blockIdx.y == 0) pattern_tensor<kTokenOrder>(p.t[0], p);
+  else pattern_tensor<kTokenOrder>(p.t[1], p);
+}
+
 }  // namespace controls
 }  // namespace sawkv
 
@@ -352,9 +401,53 @@ int cache_append_impl(const void* k, const void* v, int64_t k_stride, int64_t v_
                 (p.n_pieces + sawkv::kThreads - 1) / sawkv::kThreads, &p, stream);
 }
 
+int pattern_impl(const void* k, const void* v, int64_t k_stride, int64_t v_stride,
+                 const int64_t* slots, int64_t T, int32_t H, int32_t D, void* k_codes,
+                 void* v_codes, void* k_scales, void* v_scales, int64_t N_pg, int32_t P,
+                 int32_t placement, void* stream) {
+  int st = check_geometry(T, H, D, N_pg, P, 128, SAWKV_ROT_NONE, slots);
+  if (st) return st;
+  if (placement != SAWKV_PLACE_SLOTS && placement != SAWKV_PLACE_TOKEN_ORDER)
+    return fail(SAWKV_EINVAL, "placement = %d invalid", placement);
+  if (placement == SAWKV_PLACE_TOKEN_ORDER && T > N_pg * P)
+    return fail(SAWKV_EINVAL, "token order needs T = %lld <= N_pg*P = %lld slots", (long long)T,
+                (long long)(N_pg * P));
+  if (T == 0) return ok();
+  if (k == nullptr && v == nullptr) return fail(SAWKV_EINVAL, "both k and v are NULL");
+  if (k && (st = check_tensor("k", k, k_stride, k_codes, k_scales, H, D))) return st;
+  if (v && (st = check_tensor("v", v, v_stride, v_codes, v_scales, H, D))) return st;
+  sawkv::AppendParams p{};
+  int n = 0;
+  if (k)
+    p.t[n++] = {static_cast<const __half*>(k), k_stride, static_cast<uint8_t*>(k_codes),
+                static_cast<__half*>(k_scales)};
+  if (v)
+    p.t[n++] = {static_cast<const __half*>(v), v_stride, static_cast<uint8_t*>(v_codes),
+                static_cast<__half*>(v_scales)};
+  p.slots = slots;
+  p.n_slots = N_pg * P;
+  p.T = (int32_t)T;
+  p.TH = (int32_t)(T * H);
+  p.H = H;
+  p.h_magic = (uint32_t)(((1u << 20) + (uint32_t)H - 1u) / (uint32_t)H);
+  const void* fn = placement == SAWKV_PLACE_SLOTS
+                       ? (const void*)&sawkv::controls::pattern_kernel<false>
+                       : (const void*)&sawkv::controls::pattern_kernel<true>;
+  return launch(fn, n, (p.TH + sawkv::kVecPerBlock - 1) / sawkv::kVecPerBlock, &p, stream);
+}
+
 }  // namespace
 
 extern "C" {
+
+int sawkv_append_pattern_control(const void* k, const void* v, int64_t k_stride,
+                                 int64_t v_stride, const int64_t* slot_mapping, int64_t T,
+                                 int32_t H, int32_t D, void* k_codes, void* v_codes,
+                                 void* k_scales, void* v_scales, int64_t N_pg, int32_t P,
+                                 int32_t placement, void* stream) {
+  return pattern_impl(k, v, k_stride, v_stride, slot_mapping, T, H, D, k_codes, v_codes,
+                      k_scales, v_scales, N_pg, P, placement, stream);
+}
 
 int sawkv_cache_append(const void* k, const void* v, int64_t k_stride, int64_t v_stride,
                        const int64_t* slot_mapping, int64_t T, int32_t H, int32_t D,

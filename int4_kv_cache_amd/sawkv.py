@@ -20,6 +20,7 @@ if not os.path.exists(LIB_PATH):
 lib = ctypes.CDLL(LIB_PATH)
 
 OK, EINVAL, EUNSUPPORTED, EALIGN, EHIP = 0, 1, 2, 3, 4
+PLACE_SLOTS, PLACE_TOKEN_ORDER = 0, 1
 ROT_NONE, ROT_K, ROT_KV = 0, 1, 2
 ROT = {"none": ROT_NONE, "k": ROT_K, "kv": ROT_KV}
 
@@ -66,6 +67,9 @@ lib.sawkv_int8_append.restype = ctypes.c_int
 lib.sawkv_int8_gather.argtypes = [_p, _p, _p, _p, _i64, _i32, _p, _i64, _i32, _i32, _p, _p, _i32,
                                   _i32, _p]
 lib.sawkv_int8_gather.restype = ctypes.c_int
+lib.sawkv_append_pattern_control.argtypes = [_p, _p, _i64, _i64, _p, _i64, _i32, _i32, _p, _p,
+                                             _p, _p, _i64, _i32, _i32, _p]
+lib.sawkv_append_pattern_control.restype = ctypes.c_int
 lib.sawkv_status_string.argtypes = [ctypes.c_int]
 lib.sawkv_status_string.restype = ctypes.c_char_p
 lib.sawkv_last_error.argtypes = []
@@ -216,6 +220,48 @@ class AppendCall:
         _check(lib.sawkv_quantize_append(*self._args, _stream(stream)))
 
 
+class _Prepared:
+    """An entry point with its arguments checked and marshalled once: calling
+    the object only launches. The tensors must stay alive and keep their
+    storage while the object is used."""
+
+    def __init__(self, fn, args, keep):
+        self._fn, self._args, self._keep = fn, args, keep
+
+    def __call__(self, stream=None):
+        _check(self._fn(*self._args, _stream(stream)))
+
+
+def NaiveAppendCall(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales):
+    """sawkv_naive_int4_append, prepared (see _Prepared)."""
+    a = _append_args(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, 128, "none")
+    return _Prepared(lib.sawkv_naive_int4_append, a[:14],
+                     (k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales))
+
+
+def PatternControlCall(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, *,
+                       placement="slots"):
+    """sawkv_append_pattern_control, prepared (see _Prepared)."""
+    a = _append_args(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, 128, "none")
+    place = {"slots": PLACE_SLOTS, "token_order": PLACE_TOKEN_ORDER}[placement]
+    return _Prepared(lib.sawkv_append_pattern_control, a[:14] + (place,),
+                     (k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales))
+
+
+def GatherCall(k_codes, v_codes, k_scales, v_scales, slot_mapping, k_out, v_out, *, h=128,
+               rot="kv"):
+    """sawkv_dequant_gather into given outputs, prepared (see _Prepared)."""
+    N_pg, P, H, D, T, k_out, v_out = _gather_args(k_codes, v_codes, k_scales, v_scales,
+                                                  slot_mapping, k_out, v_out, k_out is not None,
+                                                  v_out is not None)
+    want_k, want_v = k_out is not None, v_out is not None
+    a = (_addr(k_codes) if want_k else None, _addr(v_codes) if want_v else None,
+         _addr(k_scales) if want_k else None, _addr(v_scales) if want_v else None,
+         N_pg, P, _addr(slot_mapping), T, H, D, _addr(k_out), _addr(v_out), h, _rot(rot))
+    return _Prepared(lib.sawkv_dequant_gather, a,
+                     (k_codes, v_codes, k_scales, v_scales, slot_mapping, k_out, v_out))
+
+
 def quantize_append_layers(kv, slot_mapping, pools, *, h=128, rot="kv", stream=None):
     """One launch for several layers of a decode step
     (sawkv_quantize_append_layers). kv: list of (k, v) per layer (k or v may
@@ -276,6 +322,16 @@ def naive_int4_append(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, 
     _check(lib.sawkv_naive_int4_append(*a[:14], _stream(stream)))
 
 
+def append_pattern_control(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, *,
+                           placement="slots", stream=None):
+    """The INT4 append's loads and stores with no arithmetic of the method
+    (sawkv_append_pattern_control): placement "slots" writes where the append
+    writes, "token_order" writes row t*H + head instead."""
+    a = _append_args(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, 128, "none")
+    place = {"slots": PLACE_SLOTS, "token_order": PLACE_TOKEN_ORDER}[placement]
+    _check(lib.sawkv_append_pattern_control(*a[:14], place, _stream(stream)))
+
+
 def _gather_args(k_codes, v_codes, k_scales, v_scales, slot_mapping, k_out, v_out, want_k,
                  want_v):
     if not (want_k or want_v):
@@ -333,14 +389,16 @@ def attention_workspace_size(B, Hq, H, max_context, D=128):
     return n.value
 
 
-def _attention_args(q, pools, block_tables, context_lens, max_context, h, rot, sm_scale, out,
-                    workspace):
+def _attention_common(q, pools, block_tables, context_lens, max_context, h, rot, sm_scale,
+                      out):
+    """Checked and marshalled arguments of sawkv_decode_attention up to `out`
+    (the workspace arguments excluded), out, and the workspace bytes needed."""
     k_codes, v_codes, k_scales, v_scales = pools
     N_pg, P, H, half = _pool_geometry(k_codes, k_scales)
     if tuple(_pool_geometry(v_codes, v_scales)) != (N_pg, P, H, half):
         raise ValueError("K and V pools must have the same shape")
     D = 2 * half
-    _on_gpu(q, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens, out, workspace)
+    _on_gpu(q, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens, out)
     if q.dtype != torch.float16 or q.dim() != 3 or q.shape[2] != D or q.stride(2) != 1 \
             or (q.shape[1] > 1 and q.stride(1) != D):
         raise ValueError("q must be fp16 [B, Hq, D] with unit channel stride and head stride D")
@@ -356,16 +414,25 @@ def _attention_args(q, pools, block_tables, context_lens, max_context, h, rot, s
     if out.dtype != torch.float16 or tuple(out.shape) != (B, Hq, D) or not out.is_contiguous():
         raise ValueError("out must be contiguous fp16 [B, Hq, D]")
     need = attention_workspace_size(B, Hq, H, max_context, D)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     if sm_scale is None:
         sm_scale = 1.0 / float(D) ** 0.5
     bt_stride = block_tables.stride(0) if B > 0 else block_tables.shape[1]
-    return (_addr(q), q.stride(0) if B > 0 else Hq * D, _addr(k_codes), _addr(v_codes),
+    args = (_addr(q), q.stride(0) if B > 0 else Hq * D, _addr(k_codes), _addr(v_codes),
             _addr(k_scales), _addr(v_scales), N_pg, P, _addr(block_tables), bt_stride,
             _addr(context_lens), B, Hq, H, D, max_context, float(sm_scale), h, _rot(rot),
-            _addr(out), _addr(workspace), workspace.numel() * workspace.element_size()), \
-        out, workspace
+            _addr(out))
+    return args, out, need
+
+
+def _attention_args(q, pools, block_tables, context_lens, max_context, h, rot, sm_scale, out,
+                    workspace):
+    args, out, need = _attention_common(q, pools, block_tables, context_lens, max_context, h,
+                                        rot, sm_scale, out)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _on_gpu(q, workspace)
+    return args + (_addr(workspace), workspace.numel() * workspace.element_size()), out, \
+        workspace
 
 
 def decode_attention(q, pools, block_tables, context_lens, max_context, *, h=128, rot="k",

@@ -378,3 +378,27 @@ def test_input_stride_below_row_is_rejected_by_every_append(lib, stride, which):
     assert ctl(lib, "append8", **kw) == EINVAL
     assert ctl(lib, "cache", **kw) == EINVAL
     assert b"stride" in lib.sawkv_last_error()
+
+
+def test_pattern_control_validation(lib):
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    f = lib.sawkv_append_pattern_control
+    f.argtypes = [p, p, i64, i64, p, i64, i32, i32, p, p, p, p, i64, i32, i32, p]
+
+    def call(**kw):
+        a = dict(k=K, v=V, ks=1024, vs=1024, slots=S, T=64, H=8, D=128, kc=KC, vc=VC, kss=KS,
+                 vss=VS, npg=16, P=16, place=0)
+        a.update(kw)
+        return f(a["k"], a["v"], a["ks"], a["vs"], a["slots"], a["T"], a["H"], a["D"], a["kc"],
+                 a["vc"], a["kss"], a["vss"], a["npg"], a["P"], a["place"], None)
+
+    assert call(place=2) == EINVAL
+    assert call(place=-1) == EINVAL
+    assert call(place=1, T=300, npg=16, P=16) == EINVAL       # token order needs T <= N_pg*P
+    assert b"token order" in lib.sawkv_last_error()
+    assert call(ks=-8) == EINVAL
+    assert call(k=K + 8) == EALIGN
+    assert call(D=64) == EUNSUPPORTED
+    assert call(k=None, v=None) == EINVAL
+    assert call(T=0, k=None, v=None, slots=None) == OK
+

@@ -147,3 +147,52 @@ def test_cache_append_copies_rows(env, dtype):
     O.cache_append(bits_k[:, H:2 * H], bits_k[:, 2 * H:], slots, want_k, want_v)
     assert kc.view(torch.int16).cpu().numpy().view(np.uint16).tobytes() == want_k.tobytes()
     assert vc.view(torch.int16).cpu().numpy().view(np.uint16).tobytes() == want_v.tobytes()
+
+
+# ---- access-pattern control of the INT4 append ----
+
+def pattern_rows(x):
+    """What sawkv_append_pattern_control writes per vector (its documented
+    definition, no method arithmetic): word c of the 64-byte row = xor of the
+    four uint32 words of the input row's 16-byte piece c; value bits = word 0
+    xor (word 0 >> 16), low 16 bits."""
+    T, H, D = x.shape
+    w = np.ascontiguousarray(x).view(np.uint32).reshape(T, H, 16, 4)
+    row = w[..., 0] ^ w[..., 1] ^ w[..., 2] ^ w[..., 3]
+    val = ((row[..., 0] ^ (row[..., 0] >> 16)) & 0xFFFF).astype(np.uint16)
+    return row.astype(np.uint32).view(np.uint8).reshape(T, H, 64), val
+
+
+@pytest.mark.parametrize("placement", ["slots", "token_order"])
+@pytest.mark.parametrize("H,T", [(8, 1000), (3, 77)])
+def test_append_pattern_control(env, placement, H, T):
+    """The control writes its documented bytes to the append's rows (or to
+    token order) and nothing else."""
+    torch, S = env
+    rng = np.random.default_rng(T + H)
+    k = rng.standard_normal((T, H, 128)).astype(np.float16)
+    v = rng.standard_t(4, (T, H, 128)).astype(np.float16)
+    n_pg, P = -(-T // 16) + 3, 16
+    n_slots = n_pg * P
+    slots = slots_with_holes(rng, T, n_slots)
+    say(f"pattern control {placement} H={H} T={T}")
+    dk, dv, ds = (torch.from_numpy(a).cuda() for a in (k, v, slots))
+    pools = S.alloc_pools(n_pg, P, H, 128, "cuda", code_fill=0xAA, scale_bits_fill=-1)
+    S.append_pattern_control(dk, dv, ds, *pools, placement=placement)
+    torch.cuda.synchronize()
+    got = [p.cpu().numpy().reshape(n_slots, H, -1) if i < 2 else
+           p.cpu().numpy().view(np.uint16).reshape(n_slots, H) for i, p in enumerate(pools)]
+    if placement == "slots":
+        ok = (slots >= 0) & (slots < n_slots)
+        rows = slots[ok]
+    else:
+        ok = np.ones(T, bool)
+        rows = np.arange(T)
+    for x, codes, vals in ((k, got[0], got[2]), (v, got[1], got[3])):
+        want_rows, want_vals = pattern_rows(x)
+        want_c = np.full((n_slots, H, 64), 0xAA, np.uint8)
+        want_v = np.full((n_slots, H), 0xFFFF, np.uint16)
+        want_c[rows] = want_rows[ok]
+        want_v[rows] = want_vals[ok]
+        assert codes.tobytes() == want_c.tobytes()
+        assert vals.tobytes() == want_v.tobytes()
