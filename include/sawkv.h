@@ -322,6 +322,37 @@ int sawkv_decode_attention(const void* q, int64_t q_stride,
                            void* out, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/*
+ * sawkv_decode_attention for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, arguments, validation and result as
+ * sawkv_decode_attention, without the workspace arguments. The partials live
+ * in a static device array of SAWKV_NOALLOC_MAX_BYTES inside the library, one
+ * copy per GPU, held until the process ends; its address is looked up on the
+ * first call on a device (the device of `stream`). The call allocates and
+ * frees nothing.
+ *   - Sizes whose workspace (sawkv_decode_attention_workspace_size) exceeds
+ *     SAWKV_NOALLOC_MAX_BYTES return SAWKV_EUNSUPPORTED, nothing launched
+ *     (128 MiB holds e.g. 256 sequences of up to 8000 tokens with 32 query
+ *     heads, or 64 sequences of 32768).
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (on different streams, or from different threads
+ *     without ordering) race and give undefined results. Calls ordered on one
+ *     stream are safe. Nothing in the array needs to start at zero.
+ */
+#define SAWKV_NOALLOC_MAX_BYTES ((size_t)128 << 20)
+
+int sawkv_decode_attention_noalloc(const void* q, int64_t q_stride,
+                                   const void* k_codes, const void* v_codes,
+                                   const void* k_scales, const void* v_scales,
+                                   int64_t N_pg, int32_t P,
+                                   const int32_t* block_tables, int64_t bt_stride,
+                                   const int32_t* context_lens,
+                                   int64_t B, int32_t Hq, int32_t H, int32_t D,
+                                   int64_t max_context, float sm_scale,
+                                   int32_t h, int32_t rot_mode,
+                                   void* out, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* sawkv_status_string(int status);
 

@@ -58,6 +58,8 @@
 
 #include <math.h>
 #include <stdint.h>
+
+#include <mutex>
 #include <stdio.h>
 
 #include "sawkv.h"
@@ -1406,9 +1408,76 @@ int attention_impl(const void* q, int64_t q_stride, const void* k_codes, const v
   return ok();
 }
 
+// ---- the entry point that allocates nothing ----
+//
+// For callers that cannot allocate device memory (code under graph capture,
+// tight serving loops): the partials live in a file-scope device array of
+// kScratchBytes, one copy per GPU, held until the process ends. Host code
+// never uses the array's name as an address: its device address is looked up
+// once per device with hipGetSymbolAddress (with that device current) and
+// kept in g_scratch[device].
+constexpr size_t kScratchBytes = SAWKV_NOALLOC_MAX_BYTES;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that runs `stream`.
+int scratch_for(hipStream_t stream, void** ptr) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SAWKV_EHIP, "device of the stream: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SAWKV_EUNSUPPORTED, "device %d outside the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess)
+      return fail(SAWKV_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(SAWKV_EHIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess && e2 != hipSuccess)
+        return fail(SAWKV_EHIP, "hipSetDevice(%d): %s", cur, hipGetErrorString(e2));
+    }
+    if (e != hipSuccess || p == nullptr)
+      return fail(SAWKV_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return SAWKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int sawkv_decode_attention_noalloc(const void* q, int64_t q_stride, const void* k_codes,
+                                   const void* v_codes, const void* k_scales,
+                                   const void* v_scales, int64_t N_pg, int32_t P,
+                                   const int32_t* block_tables, int64_t bt_stride,
+                                   const int32_t* context_lens, int64_t B, int32_t Hq,
+                                   int32_t H, int32_t D, int64_t max_context, float sm_scale,
+                                   int32_t h, int32_t rot_mode, void* out, void* stream) {
+  int st = check_attn_sizes(B, Hq, H, D, max_context);
+  if (st) return st;
+  const size_t need = make_layout(B, Hq, H, max_context).total;
+  if (need > kScratchBytes)
+    return fail(SAWKV_EUNSUPPORTED,
+                "these sizes need %zu bytes of partials, more than the %zu-byte static scratch "
+                "(use sawkv_decode_attention with a workspace)", need, kScratchBytes);
+  void* ws = nullptr;
+  if (B > 0 && (st = scratch_for(reinterpret_cast<hipStream_t>(stream), &ws))) return st;
+  return attention_impl(q, q_stride, k_codes, v_codes, k_scales, v_scales, N_pg, P,
+                        block_tables, bt_stride, context_lens, B, Hq, H, D, max_context,
+                        sm_scale, h, rot_mode, out, ws, kScratchBytes, stream);
+}
 
 int sawkv_decode_attention_workspace_size(int64_t B, int32_t Hq, int32_t H, int32_t D,
                                           int64_t max_context, size_t* bytes) {

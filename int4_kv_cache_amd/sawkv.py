@@ -58,6 +58,11 @@ lib.sawkv_decode_attention.argtypes = [_p, _i64, _p, _p, _p, _p, _i64, _i32, _p,
                                        _i64, _i32, _i32, _i32, _i64, ctypes.c_float, _i32, _i32,
                                        _p, _p, ctypes.c_size_t, _p]
 lib.sawkv_decode_attention.restype = ctypes.c_int
+lib.sawkv_decode_attention_noalloc.argtypes = [_p, _i64, _p, _p, _p, _p, _i64, _i32, _p, _i64,
+                                               _p, _i64, _i32, _i32, _i32, _i64, ctypes.c_float,
+                                               _i32, _i32, _p, _p]
+lib.sawkv_decode_attention_noalloc.restype = ctypes.c_int
+NOALLOC_MAX_BYTES = 128 << 20    # SAWKV_NOALLOC_MAX_BYTES
 lib.sawkv_cache_append.argtypes = [_p, _p, _i64, _i64, _p, _i64, _i32, _i32, _p, _p, _i64,
                                    _i32, _p]
 lib.sawkv_cache_append.restype = ctypes.c_int
@@ -443,6 +448,17 @@ def decode_attention(q, pools, block_tables, context_lens, max_context, *, h=128
     args, out, _ = _attention_args(q, pools, block_tables, context_lens, max_context, h, rot,
                                    sm_scale, out, workspace)
     _check(lib.sawkv_decode_attention(*args, _stream(stream)))
+    return out
+
+
+def decode_attention_noalloc(q, pools, block_tables, context_lens, max_context, *, h=128,
+                             rot="k", sm_scale=None, out=None, stream=None):
+    """sawkv_decode_attention without a workspace: the library's static
+    per-GPU scratch holds the partials (sawkv_decode_attention_noalloc).
+    Calls that overlap in time on one GPU race. Returns out."""
+    args, out, _ = _attention_common(q, pools, block_tables, context_lens, max_context, h, rot,
+                                     sm_scale, out)
+    _check(lib.sawkv_decode_attention_noalloc(*args, _stream(stream)))
     return out
 
 

@@ -402,3 +402,29 @@ def test_pattern_control_validation(lib):
     assert call(k=None, v=None) == EINVAL
     assert call(T=0, k=None, v=None, slots=None) == OK
 
+
+def test_noalloc_attention_validation(lib):
+    """The no-allocation decode attention: size checks happen before any HIP
+    call; sizes whose partials exceed the static scratch are refused."""
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    f = lib.sawkv_decode_attention_noalloc
+    f.argtypes = [p, i64, p, p, p, p, i64, i32, p, i64, p, i64, i32, i32, i32, i64,
+                  ctypes.c_float, i32, i32, p, p]
+
+    def call(**kw):
+        a = dict(q=Q, qs=32 * 128, kc=KC, vc=VC, kss=KS, vss=VS, npg=64, P=16, bt=BT,
+                 bts=1 << 20, cl=CL, B=4, Hq=32, H=8, D=128, maxc=1000, sm=0.088, h=128, rot=1,
+                 out=OUT)
+        a.update(kw)
+        return f(a["q"], a["qs"], a["kc"], a["vc"], a["kss"], a["vss"], a["npg"], a["P"],
+                 a["bt"], a["bts"], a["cl"], a["B"], a["Hq"], a["H"], a["D"], a["maxc"],
+                 a["sm"], a["h"], a["rot"], a["out"], None)
+
+    st, need = attn_ws(lib, B=64, maxc=1 << 24)
+    assert st == OK and need > 128 << 20
+    assert call(B=64, maxc=1 << 24) == EUNSUPPORTED
+    assert b"scratch" in lib.sawkv_last_error()
+    assert call(Hq=24) == EUNSUPPORTED
+    assert call(B=-1) == EINVAL
+    assert call(B=0, q=None, kc=None, vc=None, kss=None, vss=None, bt=None, cl=None,
+                out=None) == OK
