@@ -24,7 +24,8 @@ def test_traffic_record_follows_the_source_hash(monkeypatch):
     import bench
     with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
         rec = json.load(f)
-    for name, srcs in (("prefill", bench.KERNEL_SRC), ("attn", bench.ATTN_SRC)):
+    for name, srcs in (("long", bench.KERNEL_SRC), ("prefill", bench.KERNEL_SRC),
+                       ("attn", bench.ATTN_SRC)):
         ent = rec[name]
         monkeypatch.setattr(bench, "kernel_source_hash", lambda s=None, h=ent["kernel_source_hash"]: h)
         assert bench.measured_traffic(name, srcs) == ent["bytes_per_launch"]
@@ -32,12 +33,12 @@ def test_traffic_record_follows_the_source_hash(monkeypatch):
         assert bench.measured_traffic(name, srcs) is None
 
 
-@pytest.mark.parametrize("name", ["prefill", "attn"])
+@pytest.mark.parametrize("name", ["long", "prefill", "attn"])
 def test_traffic_record_is_consistent(name):
     with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
         ent = json.load(f)[name]
     kib = 1024
-    if name == "prefill":
+    if name in ("long", "prefill"):
         got = (ent["fetch_size_kib_per_dispatch"] * ent["fetch_scale"]
                + ent["write_size_kib_per_dispatch"] * ent["write_scale"]) * kib
     else:
