@@ -10,15 +10,18 @@
 // rotated key R^T y:  q . (R^T y) = (R q) . y.  The query is rotated once, and
 // no key is ever un-rotated; the value side is un-rotated once per output.
 //
-// Three kernels on the caller's stream, with a caller-provided workspace:
+// Two launches on the caller's stream, sharing a caller-provided workspace:
 //
-//  prep     one wave per (sequence, KV head): q' = R q (if keys are rotated),
-//           scaled by sm_scale * log2(e) and by a power of two 2^sigma that
-//           puts max |q'| in [2^13, 2^14); each value split into fp16
-//           hi + lo and laid out as the B operand of the score MFMAs.
-//  chunk    one wave per (sequence, chunk of C tokens, KV head): scores on
-//           the matrix cores straight from the packed nibbles, an online
-//           softmax, and P.V on the matrix cores; writes the chunk's partial
+//  chunk    one wave per (sequence, chunk of C tokens, pair of KV heads) when
+//           H is even and there are at most four queries per KV head (a
+//           wave then reads whole 128-byte lines: both heads' 64-byte rows
+//           of a token), else per (sequence, chunk, KV head). The wave first
+//           prepares its queries: q' = R q (if keys are rotated), scaled by
+//           sm_scale * log2(e) and by a power of two 2^sigma that puts
+//           max |q'| in [2^13, 2^14), each value split into fp16 hi + lo and
+//           laid out as the B operand of the score MFMAs. Then scores on the
+//           matrix cores straight from the packed nibbles, an online softmax,
+//           and P.V on the matrix cores; it writes the chunk's partial
 //           (reference exponent, denominator, unnormalised output).
 //  combine  16 lanes per (sequence, query head): merge the chunks (four
 //           quads, each over every fourth chunk), divide, un-rotate V (if
@@ -204,6 +207,31 @@ __device__ __forceinline__ QueryRaw<G, PAIR> load_query(const QueryParams& p, in
   } else {
 #pragma unroll
     for (int m = 0; m < R::CPL / 2; ++m) raw.w[m] = reinterpret_cast<const uint32_t*>(row)[m];
+  }
+  return raw;
+}
+
+// Head pairs with GR <= 4 query heads per KV head: the wave always holds 4
+// query slots per head (8 in all, the layout prepare_query expects). Slot i
+// of head hh (hh = 0, 1) is query (2 hp + hh) GR + min(i, GR - 1): with
+// GR < 4 the spare slots repeat the head's last query, and their results are
+// never written.
+template <int GR>
+__device__ __forceinline__ QueryRaw<4, true> load_query_pair(const QueryParams& p, int64_t b,
+                                                            int hp, int lane) {
+  using R = QueryRaw<4, true>;
+  constexpr int LQ = 64 / R::NQ;
+  const int g = lane / LQ, j = lane % LQ;
+  const int qi = (2 * hp + (g >> 2)) * GR + min(g & 3, GR - 1);
+  const __half* row = p.q + b * p.q_stride + (int64_t)qi * kD + j * R::CPL;
+  R raw;
+#pragma unroll
+  for (int c = 0; c < R::CPL / 8; ++c) {
+    const uint4 w = reinterpret_cast<const uint4*>(row)[c];
+    raw.w[4 * c] = w.x;
+    raw.w[4 * c + 1] = w.y;
+    raw.w[4 * c + 2] = w.z;
+    raw.w[4 * c + 3] = w.w;
   }
   return raw;
 }
@@ -700,7 +728,7 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// chunk, head pairs (G = 4): one wave per (sequence, chunk, pair of KV heads)
+// chunk, head pairs (G <= 4): one wave per (sequence, chunk, pair of KV heads)
 // ---------------------------------------------------------------------------
 //
 // The two heads of a pair hold the two halves of one 128-byte cache line of
@@ -869,9 +897,15 @@ __device__ __forceinline__ void compute_pair_step(const StepRegs& r, const uint3
   }
 }
 
-template <bool EARLY, bool STREAM>
+// GR: query heads per KV head (1, 2 or 4). The wave computes 4 query slots
+// per head whatever GR is (see load_query_pair); with GR = 1 or 2 the spare
+// slots repeat a query: the extra arithmetic is hidden behind the loads, and
+// the wave still reads whole lines. (Eight queries per head do not fit this
+// layout; they run the single-head kernel.)
+template <int GR, bool EARLY, bool STREAM>
 __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
   constexpr int G = 4;
+  static_assert(GR == 1 || GR == 2 || GR == 4, "queries per KV head");
   // STREAM: the call reads a pool several times larger than the last-level
   // cache, so the code loads are nontemporal and the stream does not displace
   // lines that are reused. Each wave reads whole 128-byte lines (two heads'
@@ -916,7 +950,7 @@ __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
   const int pages = lane < n_blk ? p.block_tables[(int64_t)b * p.bt_stride + blk0 + lane] : -1;
   // the query's load goes out between the page ids and the first step, so
   // each wait takes only what it needs (loads complete in issue order)
-  const QueryRaw<G, true> qraw = load_query<G, true>(p.qp, b, hp, lane);
+  const QueryRaw<G, true> qraw = load_query_pair<GR>(p.qp, b, hp, lane);
   const bool head_ok = (n >> 3) == (g & 1);
 
   PairLanes ln;
@@ -997,23 +1031,25 @@ __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
   for (int qc = 0; qc < 8; ++qc)
     Wq[qc] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, W),
                                                                  8 * (qc >> 2) + (qc & 3)));
-  const int64_t head0 = (int64_t)part * p.Hq + (int64_t)h0 * G;
+  // query slot j of head hh is query head (h0 + hh) GR + j; spare slots
+  // (j >= GR) are not written
+  const int64_t head0 = (int64_t)part * p.Hq + (int64_t)h0 * GR;
   if ((g & 1) == 0) {                       // g = 0: head 0, g = 2: head 1
     const int hh = g >> 1;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < (GR < 4 ? GR : 4); ++j) {
       const float Wv = hh ? Wq[4 + j] : Wq[j];
       float vals[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k)
         vals[k] = os[k][j] * ((k & 1) ? 1048576.0f : 16777216.0f) - 8.0f * Wv;
-      f4_t* dst = reinterpret_cast<f4_t*>(p.part_o + (head0 + 4 * hh + j) * kD + 8 * n);
+      f4_t* dst = reinterpret_cast<f4_t*>(p.part_o + (head0 + GR * hh + j) * kD + 8 * n);
       dst[0] = f4_t{vals[0], vals[1], vals[2], vals[3]};
       dst[1] = f4_t{vals[4], vals[5], vals[6], vals[7]};
     }
   }
-  if (g == 0 && (n & 4) == 0) {
-    const int64_t qrow = head0 + 4 * (n >> 3) + (n & 3);
+  if (g == 0 && (n & 4) == 0 && (n & 3) < GR) {
+    const int64_t qrow = head0 + GR * (n >> 3) + (n & 3);
     p.part_ml[qrow * 2] = a.m == -INFINITY ? -INFINITY : a.mref;
     p.part_ml[qrow * 2 + 1] = l;
   }
@@ -1273,10 +1309,13 @@ const void* const kChunk[2][4] = {
      (void*)&attn_chunk_kernel<4, false>, (void*)&attn_chunk_kernel<8, false>},
     {(void*)&attn_chunk_kernel<1, true>, (void*)&attn_chunk_kernel<2, true>,
      (void*)&attn_chunk_kernel<4, true>, (void*)&attn_chunk_kernel<8, true>}};
-// [first-step order][nontemporal code loads]
-const void* const kChunkPair[2][2] = {
-    {(void*)&attn_chunk_pair_kernel<false, false>, (void*)&attn_chunk_pair_kernel<false, true>},
-    {(void*)&attn_chunk_pair_kernel<true, false>, (void*)&attn_chunk_pair_kernel<true, true>}};
+// [G index][first-step order][nontemporal code loads]
+#define SAWKV_PAIR(GR)                                                                           \
+  {{(void*)&attn_chunk_pair_kernel<GR, false, false>,                                           \
+    (void*)&attn_chunk_pair_kernel<GR, false, true>},                                           \
+   {(void*)&attn_chunk_pair_kernel<GR, true, false>, (void*)&attn_chunk_pair_kernel<GR, true, true>}}
+const void* const kChunkPair[3][2][2] = {SAWKV_PAIR(1), SAWKV_PAIR(2), SAWKV_PAIR(4)};
+#undef SAWKV_PAIR
 
 // A grid of at most four rounds of resident chunk waves (3 per SIMD on 256
 // compute units) issues each wave's first loads before its query
@@ -1352,8 +1391,14 @@ int attention_impl(const void* q, int64_t q_stride, const void* k_codes, const v
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
-  // four queries per head and an even head count: heads are processed in pairs
-  const bool pair = G == 4 && H % 2 == 0;
+  // an even head count and at most four queries per head: heads are
+  // processed in pairs, so that every wave reads whole 128-byte lines (the
+  // two heads' 64-byte rows of a token). Measured at 256 sequences: 8 query
+  // heads 257 -> 228 us, 16 query heads 263 -> 232 us against the single-head
+  // kernel; for 8 queries per head, two waves per pair (each with half the
+  // queries, meeting in the L2) took 379 us against 285, so that case keeps
+  // the single-head kernel.
+  const bool pair = H % 2 == 0 && G <= 4;
   const int32_t groups = pair ? H / 2 : H;
 
   sawkv::attn::ChunkParams cp{};
@@ -1384,7 +1429,8 @@ int attention_impl(const void* q, int64_t q_stride, const void* k_codes, const v
   const int early = chunk_blocks <= kEarlyIssueBlocks ? 1 : 0;
   const bool streamed = (double)B * (double)max_context * (double)H * 132.0 > kStreamPoolBytes;
   if (max_context > 0 &&
-      (st = launch64(pair ? kChunkPair[early][streamed ? 1 : 0] : kChunk[early][g_index(G)],
+      (st = launch64(pair ? kChunkPair[g_index(G)][early][streamed ? 1 : 0]
+                          : kChunk[early][g_index(G)],
                      chunk_blocks, &cp, s)))
     return st;
 

@@ -159,10 +159,13 @@ def test_few_sequences_long_contexts(env, rot, h):
     assert np.array_equal(got[1], np.zeros_like(got[1]))
 
 
-# four queries per KV head and an even H run the head-pair kernel (H = 2, 4, 6,
-# 16 besides the default 8); an odd H (4, 1) the single-head kernel
-@pytest.mark.parametrize("Hq,H", [(8, 8), (16, 8), (64, 8), (4, 1), (2, 2),
-                                  (8, 2), (16, 4), (24, 6), (64, 16)])
+# at most four queries per KV head and an even H run the head-pair kernel
+# (G = 1 and 2 with repeated query slots: (8, 8), (16, 8), (2, 2), (12, 6);
+# G = 4: (8, 2), (16, 4), (24, 6), (64, 16)); eight queries per KV head or an
+# odd H the single-head kernel ((64, 8), (4, 1), (3, 3), (6, 3), (24, 3))
+@pytest.mark.parametrize("Hq,H", [(8, 8), (16, 8), (64, 8), (4, 1), (2, 2), (12, 6),
+                                  (8, 2), (16, 4), (24, 6), (64, 16), (3, 3), (6, 3),
+                                  (24, 3)])
 def test_group_sizes(env, Hq, H):
     wl = small(Hq=Hq, H=H, wid=8 + Hq + H)
     x = W.attn_inputs(wl)
@@ -305,11 +308,12 @@ def test_long_contexts_sampled(env):
 
 @pytest.mark.parametrize("Hq", [8, 64])
 def test_full_size_other_groupings_sampled(env, Hq):
-    """The full 256-sequence pool read by one query head per KV head (G = 1)
-    and by eight (G = 8): single-head kernel on a grid deeper than four rounds
-    of resident waves (first loads after the query preparation), sampled
-    against the oracle; then the first 64 sequences (a shallow grid, first
-    loads issued before the query preparation)."""
+    """The full 256-sequence pool read by one query head per KV head (G = 1,
+    head pairs with repeated query slots) and by eight (G = 8, single-head
+    kernel), on a grid deeper than four rounds of resident waves (first loads
+    after the query preparation), sampled against the oracle; then the first
+    64 sequences (a shallow grid, first loads issued before the query
+    preparation)."""
     wl = dataclasses.replace(W.ATTN_WORKLOADS["attn"], Hq=Hq)
     x = W.attn_inputs(wl)
     L = x["context_lens"]
