@@ -571,6 +571,7 @@ def bench_concurrency(args):
 
     levels = []
     t_start = time.perf_counter()
+    settle = None
     for c in (1, 4, 16, 64, 256):
         kv_c = [(k_[:c], v_[:c]) for k_, v_ in kvs]
         app = {r: S.LayersCall(kv_c, slots[:c], pools, h=wl.h, rot=r) for r in ("k", "none")}
@@ -580,18 +581,21 @@ def bench_concurrency(args):
                                   d["context_lens"][:c], maxc, h=wa.h, rot=r)
                for r in ("k", "none")}
         res = {}
+        if settle is None:
+            settle = settle_clocks(torch, att["k"])
         for name, calls in (("append", app), ("attention", att)):
             for fn in calls.values():
                 for _ in range(20):
                     fn()
             rot, naive = [], []
             n = max(20, args.steps // 10)
-            for _ in range(7):
+            for _ in range(9):
                 naive.append(timed(calls["none"], n))
                 rot.append(timed(calls["k"], n))
             res[name] = {"rot_us": round(float(np.median(rot)) * 1e3, 3),
                          "naive_us": round(float(np.median(naive)) * 1e3, 3),
-                         "rot_over_naive": round(float(np.median(rot) / np.median(naive)), 4)}
+                         "rot_over_naive": round(float(np.median(rot) / np.median(naive)), 4),
+                         "rot_over_naive_ci95": bootstrap_ratio_ci(rot, naive)}
         step_rot = res["append"]["rot_us"] + layers * res["attention"]["rot_us"]
         step_naive = res["append"]["naive_us"] + layers * res["attention"]["naive_us"]
         levels.append({"concurrency": c, "context_tokens": int(L.sum()),
@@ -623,6 +627,7 @@ def bench_concurrency(args):
                                 "step estimate = 36-layer append + 36 x one layer's attention"),
                    "levels": [l["concurrency"] for l in levels], "parallelism": "single GPU"},
         "levels": levels,
+        "settle": settle,
         "seconds": round(wall, 1),
         "roofline": None,
         "cpu_baseline": None,
@@ -820,6 +825,10 @@ def main():
     # the committed counters cover the workloads at their own shapes only
     traffic = measured_traffic(args.workload) if not args.heads else None
     resident = read_bytes <= LLC_BYTES
+    # every timed call rewrites the same rows of codes and scales: when those
+    # rows fit the last-level cache, back-to-back calls can leave part of the
+    # writes there (the cold figures start from a flushed cache)
+    rows_bytes = wl.T * wl.H * (wl.D // 2 + 2) * 2 * layers
     out = {
         "metric": METRIC,
         "value": round(gbps, 2),
@@ -846,6 +855,7 @@ def main():
         "tokens_per_s": round(tokens / (wall_ms * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "cache_resident": resident,
+        "rewritten_rows_fit_llc": rows_bytes <= LLC_BYTES,
         "settle": settle,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
