@@ -151,23 +151,34 @@ __device__ __forceinline__ void quantize_store(const AppendTensor& A, const Appe
 // grid: the kernel is bound by HBM, and the one-shot grid keeps more waves
 // resident.)
 template <int HB>
-__device__ __forceinline__ void append_tensor(const AppendTensor& A, const AppendParams& p) {
+__device__ __forceinline__ void append_tensor(const AppendTensor& A, const AppendParams& p,
+                                              uint32_t bx) {
   const int lane = threadIdx.x & 63;
   const int lam = lane & 3;
   const int vq = lane >> 2;
   const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   WavePos w;
-  w.v0 = (blockIdx.x * kWaves + wave) * kVecPerWave;      // wave-uniform
+  w.v0 = (bx * kWaves + wave) * kVecPerWave;              // wave-uniform
   if (w.v0 >= (uint32_t)p.TH) return;
   w.t0 = w.v0 / (uint32_t)p.H;
   w.h0 = w.v0 - w.t0 * (uint32_t)p.H;
   quantize_store<HB>(A, p, fetch_batch(A, p, w, lam, vq), lam);
 }
 
+// Grid (blocks, tensors): every block of the first tensor is dispatched
+// before any of the second. Grid (2 * blocks, 1) with two tensors: the
+// tensors' blocks alternate in dispatch order (host side: only for inputs of
+// at least kAlternateBytes, see append_impl).
 template <int HB0, int HB1>
 __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p) {
-  if (blockIdx.y == 0) append_tensor<HB0>(p.t[0], p);
-  else append_tensor<HB1>(p.t[1], p);
+  if (gridDim.y == 1 && p.t[1].src != nullptr) {
+    if ((blockIdx.x & 1u) == 0) append_tensor<HB0>(p.t[0], p, blockIdx.x >> 1);
+    else append_tensor<HB1>(p.t[1], p, blockIdx.x >> 1);
+  } else if (blockIdx.y == 0) {
+    append_tensor<HB0>(p.t[0], p, blockIdx.x);
+  } else {
+    append_tensor<HB1>(p.t[1], p, blockIdx.x);
+  }
 }
 
 // Several layers of one decode step in one launch: every layer shares the
@@ -214,8 +225,8 @@ __global__ __launch_bounds__(kThreads) void append_layers_kernel(LayersParams p)
   const bool is_v = p.n_tensors == 2 ? slot_in_layer == 1 : p.only_v != 0;
   const AppendTensor A = is_v ? AppendTensor{L.v, p.v_stride, L.v_codes, L.v_scales}
                               : AppendTensor{L.k, p.k_stride, L.k_codes, L.k_scales};
-  if (slot_in_layer == 0) append_tensor<HB0>(A, p.common);
-  else append_tensor<HB1>(A, p.common);
+  if (slot_in_layer == 0) append_tensor<HB0>(A, p.common, blockIdx.x);
+  else append_tensor<HB1>(A, p.common, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -492,6 +503,20 @@ int check_output(const char* name, const void* out, const void* codes, const voi
   return SAWKV_OK;
 }
 
+// K and V blocks alternate in dispatch order when the call reads at least
+// kAlternateBytes of fp16 K and V, i.e. when the input streams from HBM at
+// several times the 256 MB last-level cache. Measured on MI355X, alternating
+// against every K block first (long-context batch of 2.1 M tokens, us per
+// launch): 8 heads (8.6 GB) 2069 vs 2089, 4 heads 1037 vs 1041, 2 heads 517 vs
+// 519, 1 head (1 GiB) 263.7 vs 264.2; below, prefill (0.54 GB) 127.0 vs 125.6
+// and 0.27 GB 61.8 vs 60.2, where it is slower. The access-pattern control
+// follows the same rule.
+constexpr int64_t kAlternateBytes = INT64_C(1) << 30;
+
+bool alternate_tensors(int64_t T, int32_t H, int32_t D) {
+  return T * (int64_t)H * D * 2 * 2 >= kAlternateBytes;
+}
+
 // kernel index: 0 = naive, 1..4 = h 16/32/64/128
 int hb_index(int32_t h, bool rot) {
   if (!rot) return 0;
@@ -504,6 +529,7 @@ int hb_index(int32_t h, bool rot) {
 namespace {
 
 using sawkv::host::aligned;
+using sawkv::host::alternate_tensors;
 using sawkv::host::check_geometry;
 using sawkv::host::check_output;
 using sawkv::host::check_tensor;
@@ -577,6 +603,8 @@ int append_impl(const void* k, const void* v, int64_t k_stride, int64_t v_stride
   p.TH = (int32_t)(T * H);
   p.H = H;
   p.h_magic = (uint32_t)(((1u << 20) + (uint32_t)H - 1u) / (uint32_t)H);
+  if (n == 2 && alternate_tensors(T, H, D))
+    return launch(kAppend[hb[0]][hb[1]], 1, 2 * append_blocks(p.TH), &p, stream);
   return launch(kAppend[hb[0]][hb[1]], n, append_blocks(p.TH), &p, stream);
 }
 

@@ -241,13 +241,14 @@ __global__ __launch_bounds__(kThreads) void cache_append_kernel(CacheParams p) {
 // (token order) instead of the mapped slot, which shows what the same loads
 // reach when the destination pages are contiguous.
 template <bool kTokenOrder>
-__device__ __forceinline__ void pattern_tensor(const AppendTensor& A, const AppendParams& p) {
+__device__ __forceinline__ void pattern_tensor(const AppendTensor& A, const AppendParams& p,
+                                               uint32_t bx) {
   const int lane = threadIdx.x & 63;
   const int lam = lane & 3;
   const int vq = lane >> 2;
   const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   WavePos w;
-  w.v0 = (blockIdx.x * kWaves + wave) * kVecPerWave;
+  w.v0 = (bx * kWaves + wave) * kVecPerWave;
   if (w.v0 >= (uint32_t)p.TH) return;
   w.t0 = w.v0 / (uint32_t)p.H;
   w.h0 = w.v0 - w.t0 * (uint32_t)p.H;
@@ -270,10 +271,18 @@ __device__ __forceinline__ void pattern_tensor(const AppendTensor& A, const Appe
   if (lam == 0) A.scales[row] = __builtin_bit_cast(__half, sbits);
 }
 
+// The same grid forms as the append (tensors' blocks alternating in
+// dispatch order when the append alternates them).
 template <bool kTokenOrder>
 __global__ __launch_bounds__(kThreads) void pattern_kernel(AppendParams p) {
-  if (blockIdx.y == 0) pattern_tensor<kTokenOrder>(p.t[0], p);
-  else pattern_tensor<kTokenOrder>(p.t[1], p);
+  if (gridDim.y == 1 && p.t[1].src != nullptr) {
+    if ((blockIdx.x & 1u) == 0) pattern_tensor<kTokenOrder>(p.t[0], p, blockIdx.x >> 1);
+    else pattern_tensor<kTokenOrder>(p.t[1], p, blockIdx.x >> 1);
+  } else if (blockIdx.y == 0) {
+    pattern_tensor<kTokenOrder>(p.t[0], p, blockIdx.x);
+  } else {
+    pattern_tensor<kTokenOrder>(p.t[1], p, blockIdx.x);
+  }
 }
 
 }  // namespace controls
@@ -433,7 +442,9 @@ int pattern_impl(const void* k, const void* v, int64_t k_stride, int64_t v_strid
   const void* fn = placement == SAWKV_PLACE_SLOTS
                        ? (const void*)&sawkv::controls::pattern_kernel<false>
                        : (const void*)&sawkv::controls::pattern_kernel<true>;
-  return launch(fn, n, (p.TH + sawkv::kVecPerBlock - 1) / sawkv::kVecPerBlock, &p, stream);
+  const int64_t blocks = (p.TH + sawkv::kVecPerBlock - 1) / sawkv::kVecPerBlock;
+  if (n == 2 && sawkv::host::alternate_tensors(T, H, D)) return launch(fn, 1, 2 * blocks, &p, stream);
+  return launch(fn, n, blocks, &p, stream);
 }
 
 }  // namespace

@@ -30,6 +30,10 @@ int check_tensor(const char* name, const void* x, int64_t stride, const void* co
 // pointers non-null.
 int check_output(const char* name, const void* out, const void* codes, const void* scales);
 
+// Whether an append of both tensors dispatches their blocks alternately
+// (large inputs) rather than every first-tensor block first.
+bool alternate_tensors(int64_t T, int32_t H, int32_t D);
+
 // Kernel-table index of a tensor: 0 = not rotated, 1..4 = h 16/32/64/128.
 int hb_index(int32_t h, bool rot);
 

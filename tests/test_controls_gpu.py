@@ -164,14 +164,15 @@ def pattern_rows(x):
 
 
 @pytest.mark.parametrize("placement", ["slots", "token_order"])
-@pytest.mark.parametrize("H,T", [(8, 1000), (3, 77)])
+@pytest.mark.parametrize("H,T", [(8, 1000), (3, 77), (8, 262144)])
 def test_append_pattern_control(env, placement, H, T):
     """The control writes its documented bytes to the append's rows (or to
-    token order) and nothing else."""
+    token order) and nothing else; 262 144 tokens x 8 heads is 1 GiB of K and
+    V, where K and V blocks alternate in dispatch order."""
     torch, S = env
     rng = np.random.default_rng(T + H)
-    k = rng.standard_normal((T, H, 128)).astype(np.float16)
-    v = rng.standard_t(4, (T, H, 128)).astype(np.float16)
+    k = rng.standard_normal((T, H, 128), dtype=np.float32).astype(np.float16)
+    v = rng.standard_normal((T, H, 128), dtype=np.float32).astype(np.float16) * np.float16(3)
     n_pg, P = -(-T // 16) + 3, 16
     n_slots = n_pg * P
     slots = slots_with_holes(rng, T, n_slots)
