@@ -113,6 +113,20 @@ __device__ __forceinline__ void swap32(float& a, float& b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
 
+// max(a, b) as one v_max_f32, without the quieting of signalling NaNs that
+// fmaxf adds for operands the compiler cannot prove canonical (select and
+// lane-exchange results). Operands here are finite or -inf.
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float d;
+  asm("v_max_f32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float d;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
 // Sum (or max) over the four rows of 16 lanes; every row gets the result.
 __device__ __forceinline__ float rows_sum(float v) {
   float a = v, b = v;
@@ -125,9 +139,9 @@ __device__ __forceinline__ float rows_sum(float v) {
 __device__ __forceinline__ float rows_max(float v) {
   float a = v, b = v;
   swap16(a, b);
-  float c = fmaxf(a, b), d = fmaxf(a, b);
+  float c = max_raw(a, b), d = c;
   swap32(c, d);
-  return fmaxf(c, d);
+  return max_raw(c, d);
 }
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
@@ -474,10 +488,11 @@ __device__ __forceinline__ void compute_step(const StepRegs& r, const uint32_t (
     f4_t acc = f4_t{cinit, cinit, cinit, cinit};
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-      const uint32_t w = r.kq[T][cc] ^ 0x88888888u;
-      const uint32_t w8 = w >> 8;
-      const u4_t av = u4_t{w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu,
-                           w8 & 0x00F000F0u};
+      // u = code + 8 = nibble ^ 8, masked into the fp16 lanes (the shift
+      // is taken before the xor so each masked word is one 3-input logic op)
+      const uint32_t raw = r.kq[T][cc], raw8 = raw >> 8;
+      const u4_t av = u4_t{(raw ^ 0x88888888u) & 0x000F000Fu, (raw ^ 0x88888888u) & 0x00F000F0u,
+                           (raw8 ^ 0x00888888u) & 0x000F000Fu, (raw8 ^ 0x00888888u) & 0x00F000F0u};
       acc = mfma(av, bq[cc], acc);
     }
 #pragma unroll
@@ -490,15 +505,19 @@ __device__ __forceinline__ void compute_step(const StepRegs& r, const uint32_t (
     }
   }
   if (mask) {
+    // token 16 T + 4 g + j of the step is valid iff 4 g < t_end - t0 - 16 T - j
+    // (a per-lane value against a wave-uniform one)
+    const int rem = __builtin_amdgcn_readfirstlane(t_end - t0);
 #pragma unroll
     for (int T = 0; T < 2; ++T)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (!(r.ok[T] && t0 + 16 * T + 4 * g + j < t_end)) mu[T][j] = -INFINITY;
+        if (!(r.ok[T] && 4 * g < rem - 16 * T - j)) mu[T][j] = -INFINITY;
   }
 
-  float mx = fmaxf(fmaxf(fmaxf(mu[0][0], mu[0][1]), fmaxf(mu[0][2], mu[0][3])),
-                   fmaxf(fmaxf(mu[1][0], mu[1][1]), fmaxf(mu[1][2], mu[1][3])));
+  float mx = max3_raw(max3_raw(mu[0][0], mu[0][1], mu[0][2]),
+                      max3_raw(mu[0][3], mu[1][0], mu[1][1]),
+                      max3_raw(mu[1][2], mu[1][3], -INFINITY));
   mx = rows_max(mx);
   const bool need = n < G && mx > a.m + 32.0f;
   if (__any(need)) {
@@ -538,11 +557,12 @@ __device__ __forceinline__ void compute_step(const StepRegs& r, const uint32_t (
       w[T][j] = fmaf((float)((j & 1) ? half_hi(vw) : half_lo(vw)), pr[T][j], 0.0f);
     }
   if (mask) {
+    const int rem = __builtin_amdgcn_readfirstlane(t_end - t0);
 #pragma unroll
     for (int T = 0; T < 2; ++T)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (!(r.ok[T] && t0 + 16 * T + 4 * g + j < t_end)) pr[T][j] = w[T][j] = 0.0f;
+        if (!(r.ok[T] && 4 * g < rem - 16 * T - j)) pr[T][j] = w[T][j] = 0.0f;
   }
 #pragma unroll
   for (int T = 0; T < 2; ++T)
@@ -551,13 +571,16 @@ __device__ __forceinline__ void compute_step(const StepRegs& r, const uint32_t (
       a.l += pr[T][j];
       a.W += w[T][j];
     }
+  // w - hi (exact): one mixed-precision fma each, reading hi as fp16 (the -1
+  // is kept opaque so the fma is not folded into a convert and a subtract)
+  const float mone = opaque(-1.0f);
   u4_t A;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int T = e >> 1, j0 = 2 * (e & 1);
     const h2_t hi = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(w[T][j0], w[T][j0 + 1]));
-    const float r0 = fmaf((float)hi[0], -1.0f, w[T][j0]);
-    const float r1 = fmaf((float)hi[1], -1.0f, w[T][j0 + 1]);
+    const float r0 = fmaf((float)hi[0], mone, w[T][j0]);
+    const float r1 = fmaf((float)hi[1], mone, w[T][j0 + 1]);
     const h2_t lo = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
     A[e] = lo_rows<G>(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo));
   }
@@ -796,10 +819,11 @@ __device__ __forceinline__ void compute_pair_step(const StepRegs& r, const uint3
     f4_t acc = f4_t{cinit, cinit, cinit, cinit};
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-      const uint32_t w = r.kq[T][cc] ^ 0x88888888u;
-      const uint32_t w8 = w >> 8;
-      const u4_t av = u4_t{w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu,
-                           w8 & 0x00F000F0u};
+      // u = code + 8 = nibble ^ 8, masked into the fp16 lanes (the shift
+      // is taken before the xor so each masked word is one 3-input logic op)
+      const uint32_t raw = r.kq[T][cc], raw8 = raw >> 8;
+      const u4_t av = u4_t{(raw ^ 0x88888888u) & 0x000F000Fu, (raw ^ 0x88888888u) & 0x00F000F0u,
+                           (raw8 ^ 0x00888888u) & 0x000F000Fu, (raw8 ^ 0x00888888u) & 0x00F000F0u};
       acc = mfma(av, bq[cc], acc);
     }
 #pragma unroll
@@ -812,15 +836,19 @@ __device__ __forceinline__ void compute_pair_step(const StepRegs& r, const uint3
     }
   }
   if (mask) {
+    // token 8 T + 2 j + g / 2 of the step is valid iff g / 2 < t_end - t0 - 8 T - 2 j
+    // (a per-lane value against a wave-uniform one)
+    const int rem = __builtin_amdgcn_readfirstlane(t_end - t0);
 #pragma unroll
     for (int T = 0; T < 2; ++T)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (!(r.ok[T] && t0 + 8 * T + 2 * j + (g >> 1) < t_end)) mu[T][j] = -INFINITY;
+        if (!(r.ok[T] && (g >> 1) < rem - 8 * T - 2 * j)) mu[T][j] = -INFINITY;
   }
 
-  float mx = fmaxf(fmaxf(fmaxf(mu[0][0], mu[0][1]), fmaxf(mu[0][2], mu[0][3])),
-                   fmaxf(fmaxf(mu[1][0], mu[1][1]), fmaxf(mu[1][2], mu[1][3])));
+  float mx = max3_raw(max3_raw(mu[0][0], mu[0][1], mu[0][2]),
+                      max3_raw(mu[0][3], mu[1][0], mu[1][1]),
+                      max3_raw(mu[1][2], mu[1][3], -INFINITY));
   mx = rows_max(head_ok ? mx : -INFINITY);
   const bool need = (n & 4) == 0 && mx > a.m + 32.0f;
   if (__any(need)) {
@@ -853,11 +881,12 @@ __device__ __forceinline__ void compute_pair_step(const StepRegs& r, const uint3
       w[T][j] = fmaf((float)((j & 1) ? half_hi(vw) : half_lo(vw)), pr[T][j], 0.0f);
     }
   if (mask) {
+    const int rem = __builtin_amdgcn_readfirstlane(t_end - t0);
 #pragma unroll
     for (int T = 0; T < 2; ++T)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (!(r.ok[T] && t0 + 8 * T + 2 * j + (g >> 1) < t_end)) pr[T][j] = w[T][j] = 0.0f;
+        if (!(r.ok[T] && (g >> 1) < rem - 8 * T - 2 * j)) pr[T][j] = w[T][j] = 0.0f;
   }
 #pragma unroll
   for (int T = 0; T < 2; ++T)
@@ -866,13 +895,16 @@ __device__ __forceinline__ void compute_pair_step(const StepRegs& r, const uint3
       a.l += pr[T][j];
       a.W += w[T][j];
     }
+  // w - hi (exact): one mixed-precision fma each, reading hi as fp16 (the -1
+  // is kept opaque so the fma is not folded into a convert and a subtract)
+  const float mone = opaque(-1.0f);
   u4_t A;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int T = e >> 1, j0 = 2 * (e & 1);
     const h2_t hi = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(w[T][j0], w[T][j0 + 1]));
-    const float r0 = fmaf((float)hi[0], -1.0f, w[T][j0]);
-    const float r1 = fmaf((float)hi[1], -1.0f, w[T][j0 + 1]);
+    const float r0 = fmaf((float)hi[0], mone, w[T][j0]);
+    const float r1 = fmaf((float)hi[1], mone, w[T][j0 + 1]);
     const h2_t lo = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
     // lanes 4-7 and 12-15 of each row take the lo part from lane - 4
     const uint32_t v = (uint32_t)__builtin_amdgcn_update_dpp(
