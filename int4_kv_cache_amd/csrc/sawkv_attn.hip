@@ -13,9 +13,8 @@
 // Two launches on the caller's stream, sharing a caller-provided workspace:
 //
 //  chunk    one wave per (sequence, chunk of C tokens, pair of KV heads) when
-//           H is even and there are at most four queries per KV head (a
-//           wave then reads whole 128-byte lines: both heads' 64-byte rows
-//           of a token), else per (sequence, chunk, KV head). The wave first
+//           H is even (a wave then reads whole 128-byte lines: both heads'
+//           64-byte rows of a token), else per (sequence, chunk, KV head). The wave first
 //           prepares its queries: q' = R q (if keys are rotated), scaled by
 //           sm_scale * log2(e) and by a power of two 2^sigma that puts
 //           max |q'| in [2^13, 2^14), each value split into fp16 hi + lo and
@@ -164,15 +163,21 @@ struct QueryParams {
 // Column n of the score MFMAs' B operand holds (query of the block, part):
 //   single head (PAIR false): n < G hi of query n, G <= n < 2G lo of query n - G
 //   head pair (PAIR true, G = 4): query 4 (n / 8) + n % 4, lo when n & 4
+//   head pair (PAIR true, G = 8): query n; the hi parts form one operand and
+//                                 the lo parts a second one (split_operand)
 // where the block's queries are those of its heads in order.
 template <int G, bool PAIR>
+constexpr bool split_operand() { return PAIR && G == 8; }
+template <int G, bool PAIR>
 __device__ __forceinline__ int column_query(int n) {
-  if constexpr (PAIR) return 4 * (n >> 3) + (n & 3);
+  if constexpr (split_operand<G, PAIR>()) return n;
+  else if constexpr (PAIR) return 4 * (n >> 3) + (n & 3);
   else return n < G ? n : (n < 2 * G ? n - G : -1);
 }
 template <int G, bool PAIR>
 __device__ __forceinline__ bool column_hi(int n) {
-  if constexpr (PAIR) return (n & 4) == 0;
+  if constexpr (split_operand<G, PAIR>()) return true;
+  else if constexpr (PAIR) return (n & 4) == 0;
   else return n < G;
 }
 
@@ -225,18 +230,23 @@ __device__ __forceinline__ QueryRaw<G, PAIR> load_query(const QueryParams& p, in
   return raw;
 }
 
-// Head pairs with GR <= 4 query heads per KV head: the wave always holds 4
-// query slots per head (8 in all, the layout prepare_query expects). Slot i
-// of head hh (hh = 0, 1) is query (2 hp + hh) GR + min(i, GR - 1): with
-// GR < 4 the spare slots repeat the head's last query, and their results are
-// never written.
+// Query slots per head of the head-pair kernel: 8 for GR = 8, else 4.
 template <int GR>
-__device__ __forceinline__ QueryRaw<4, true> load_query_pair(const QueryParams& p, int64_t b,
-                                                            int hp, int lane) {
-  using R = QueryRaw<4, true>;
+constexpr int pair_slots() { return GR == 8 ? 8 : 4; }
+
+// Head pairs with GR query heads per KV head: the wave holds QS =
+// pair_slots<GR>() query slots per head (2 QS in all, the layout
+// prepare_query expects). Slot i of head hh (hh = 0, 1) is query
+// (2 hp + hh) GR + min(i, GR - 1): with GR < QS the spare slots repeat the
+// head's last query, and their results are never written.
+template <int GR>
+__device__ __forceinline__ QueryRaw<pair_slots<GR>(), true> load_query_pair(
+    const QueryParams& p, int64_t b, int hp, int lane) {
+  constexpr int QS = pair_slots<GR>();
+  using R = QueryRaw<QS, true>;
   constexpr int LQ = 64 / R::NQ;
   const int g = lane / LQ, j = lane % LQ;
-  const int qi = (2 * hp + (g >> 2)) * GR + min(g & 3, GR - 1);
+  const int qi = (2 * hp + g / QS) * GR + min(g % QS, GR - 1);
   const __half* row = p.q + b * p.q_stride + (int64_t)qi * kD + j * R::CPL;
   R raw;
 #pragma unroll
@@ -266,9 +276,11 @@ __device__ __forceinline__ QueryRaw<4, true> load_query_pair(const QueryParams& 
 template <int G, bool PAIR>
 __device__ __forceinline__ void prepare_query(const QueryParams& p, const QueryRaw<G, PAIR>& raw,
                                               int lane, float (*xs)[kD], u4_t (&bq)[4],
-                                              float& cinit_n, float& F_n) {
+                                              float& cinit_n, float& F_n, u4_t* bq_lo = nullptr) {
   constexpr int NQ = PAIR ? 2 * G : G;          // queries of the wave
-  static_assert(!PAIR || G == 4, "head pairs are laid out for 4 queries per head");
+  static_assert(!PAIR || G == 4 || G == 8, "head pairs are laid out for 4 or 8 queries per head");
+  // split_operand: bq gets the hi parts, bq_lo the lo parts of every column
+  constexpr bool kSplit = split_operand<G, PAIR>();
   constexpr int LQ = 64 / NQ;                   // lanes per query
   constexpr int CPL = kD / LQ;                  // channels per lane
   const int g = lane / LQ, j = lane % LQ;
@@ -343,31 +355,37 @@ __device__ __forceinline__ void prepare_query(const QueryParams& p, const QueryR
   __syncthreads();
 
   const int gl = lane >> 4, n = lane & 15;
-  uint32_t words[kQWords];
+  uint32_t words[kQWords], words_lo[kQWords];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int ch0 = 8 * (4 * gl + c) + e, ch1 = ch0 + 4;
-      uint32_t w = 0;
+      uint32_t w = 0, wl = 0;
       const int qi = column_query<G, PAIR>(n);
       if (qi >= 0) {
         float v[2] = {xs[qi][ch0], xs[qi][ch1]};
-        uint16_t bits[2];
+        uint16_t bits[2], bits_lo[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const _Float16 hi = (_Float16)v[k];
           const _Float16 lo = (_Float16)(v[k] - (float)hi);
           bits[k] = __builtin_bit_cast(uint16_t, column_hi<G, PAIR>(n) ? hi : lo);
+          bits_lo[k] = __builtin_bit_cast(uint16_t, lo);
         }
         w = (uint32_t)bits[0] | ((uint32_t)bits[1] << 16);
+        wl = (uint32_t)bits_lo[0] | ((uint32_t)bits_lo[1] << 16);
       }
       words[4 * c + e] = w;
+      words_lo[4 * c + e] = wl;
     }
   }
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
+  for (int k = 0; k < 4; ++k) {
     bq[k] = u4_t{words[4 * k], words[4 * k + 1], words[4 * k + 2], words[4 * k + 3]};
+    if constexpr (kSplit)
+      bq_lo[k] = u4_t{words_lo[4 * k], words_lo[4 * k + 1], words_lo[4 * k + 2], words_lo[4 * k + 3]};
+  }
   {
     const int qi = column_query<G, PAIR>(n);
     const int src = (qi >= 0 ? qi : 0) * LQ;
@@ -751,7 +769,7 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// chunk, head pairs (G <= 4): one wave per (sequence, chunk, pair of KV heads)
+// chunk, head pairs (even H): one wave per (sequence, chunk, pair of KV heads)
 // ---------------------------------------------------------------------------
 //
 // The two heads of a pair hold the two halves of one 128-byte cache line of
@@ -759,14 +777,18 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
 // tokens (one page-aligned block) of both heads, as two tiles of 8 tokens.
 //
 // Scores: MFMA row m of tile tau is token 8 tau + 2 (m % 4) + m / 8 of head
-// (m / 4) % 2; columns 0-3 / 4-7 hold the hi / lo parts of head 0's four
-// queries, 8-11 / 12-15 those of head 1. Result lane (g, n) holds rows
-// 4g + j: tokens 8 tau + 2j + g / 2 of head g % 2, so its values are useful
-// when its column belongs to that head (n / 8 == g % 2, n % 8 < 4).
+// (m / 4) % 2. With four query slots per head, columns 0-3 / 4-7 hold the
+// hi / lo parts of head 0's four queries, 8-11 / 12-15 those of head 1; with
+// eight, column n holds query n % 8 of head n / 8, hi parts in one operand
+// and lo parts in a second. Result lane (g, n) holds rows 4g + j: tokens
+// 8 tau + 2j + g / 2 of head g % 2, so its values are useful when its column
+// belongs to that head (n / 8 == g % 2; with four slots also n % 8 < 4).
 // Values: k slot (g, i = 4 tau + j) is token 8 tau + 2j + g / 2 of head g % 2,
-// so the weights sit in the same lanes as their scores; rows 0-3 / 4-7 of the
-// A operand are head 0's hi / lo weights, rows 8-11 / 12-15 head 1's, and a
-// row is zero where the slot's head is not the row's head.
+// so the weights sit in the same lanes as their scores. With four slots rows
+// 0-3 / 4-7 of the A operand are head 0's hi / lo weights, rows 8-11 / 12-15
+// head 1's; with eight, row n is query n % 8 of head n / 8 and the hi and lo
+// weights are two A operands. A row is zero where the slot's head is not the
+// row's head.
 
 struct PairLanes {
   uint32_t k_off[2];   // byte offsets of the lane's K code bytes, tiles 0 and 1
@@ -808,15 +830,24 @@ __device__ __forceinline__ void load_pair_step(const ChunkParams& p, StepRegs& r
 // One 16-token step of a head pair. ks[tau] / vs[tau]: the K / V scales of the
 // lane's rows (tokens 8 tau + 2j + g / 2, head g % 2, j = 0..3) as two dwords
 // of fp16 pairs. head_ok: the lane's column belongs to its rows' head.
+//
+// QS = 8 query slots per head: the score columns are the 16 queries (bq their
+// hi parts, bq_lo their lo parts, one MFMA chain each, added per element as
+// the hi and lo columns are with QS = 4), and the value rows are the 16
+// queries too, the hi and the lo weights entering as two MFMAs into the same
+// accumulator.
+template <int QS>
 __device__ __forceinline__ void compute_pair_step(const StepRegs& r, const uint32_t (&ks)[2][2],
                                                   const uint32_t (&vs)[2][2], const u4_t (&bq)[4],
-                                                  float cinit, float F, float F4, Acc<4>& a,
-                                                  int g, int n, bool head_ok, int t0, int t_end,
-                                                  bool mask) {
+                                                  const u4_t (&bq_lo)[4], float cinit, float F,
+                                                  float F4, Acc<QS>& a, int g, int n, bool head_ok,
+                                                  int t0, int t_end, bool mask) {
+  static_assert(QS == 4 || QS == 8, "query slots per head");
   float lam[2][4], mu[2][4];
 #pragma unroll
   for (int T = 0; T < 2; ++T) {
     f4_t acc = f4_t{cinit, cinit, cinit, cinit};
+    f4_t acl = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
       // u = code + 8 = nibble ^ 8, masked into the fp16 lanes (the shift
@@ -825,10 +856,11 @@ __device__ __forceinline__ void compute_pair_step(const StepRegs& r, const uint3
       const u4_t av = u4_t{(raw ^ 0x88888888u) & 0x000F000Fu, (raw ^ 0x88888888u) & 0x00F000F0u,
                            (raw8 ^ 0x00888888u) & 0x000F000Fu, (raw8 ^ 0x00888888u) & 0x00F000F0u};
       acc = mfma(av, bq[cc], acc);
+      if constexpr (QS == 8) acl = mfma(av, bq_lo[cc], acl);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float sc = acc[j] + row_shl<4>(acc[j]);
+      const float sc = QS == 8 ? acc[j] + acl[j] : acc[j] + row_shl<4>(acc[j]);
       const uint32_t kw = ks[T][j >> 1], vw = vs[T][j >> 1];
       lam[T][j] = fmaf((float)((j & 1) ? half_hi(kw) : half_lo(kw)), sc, 0.0f);
       const float ub = (float)((j & 1) ? (vw >> 24) : ((vw >> 8) & 0xFFu));
@@ -850,20 +882,27 @@ __device__ __forceinline__ void compute_pair_step(const StepRegs& r, const uint3
                       max3_raw(mu[0][3], mu[1][0], mu[1][1]),
                       max3_raw(mu[1][2], mu[1][3], -INFINITY));
   mx = rows_max(head_ok ? mx : -INFINITY);
-  const bool need = (n & 4) == 0 && mx > a.m + 32.0f;
+  const bool need = (QS == 8 || (n & 4) == 0) && mx > a.m + 32.0f;
   if (__any(need)) {
     const float mn = need ? mx : a.m;
     const float alpha = need ? __builtin_amdgcn_exp2f((a.m - mn) * 0.25f) : 1.0f;
     a.l *= alpha;
     a.W *= alpha;
-    float al[8];
+    constexpr int NA = 2 * QS;
+    float al[NA];
 #pragma unroll
-    for (int qc = 0; qc < 8; ++qc)
-      al[qc] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                             __builtin_bit_cast(int, alpha), 8 * (qc >> 2) + (qc & 3)));
+    for (int qc = 0; qc < NA; ++qc)
+      al[qc] = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha),
+                                           QS == 8 ? qc : 8 * (qc >> 2) + (qc & 3)));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float f = (g >> 1) ? al[4 + j] : al[j];     // rows 4g + j: head g / 2, query j
+      // QS = 4: rows 4g + j are head g / 2, query j; QS = 8: query 4g + j
+      float f;
+      if constexpr (QS == 8)
+        f = g == 0 ? al[j] : g == 1 ? al[4 + j] : g == 2 ? al[8 + j] : al[12 + j];
+      else
+        f = (g >> 1) ? al[4 + j] : al[j];
 #pragma unroll
       for (int k = 0; k < 8; ++k) a.o[k][j] *= f;
     }
@@ -898,7 +937,7 @@ __device__ __forceinline__ void compute_pair_step(const StepRegs& r, const uint3
   // w - hi (exact): one mixed-precision fma each, reading hi as fp16 (the -1
   // is kept opaque so the fma is not folded into a convert and a subtract)
   const float mone = opaque(-1.0f);
-  u4_t A;
+  u4_t A, Alo;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int T = e >> 1, j0 = 2 * (e & 1);
@@ -906,11 +945,16 @@ __device__ __forceinline__ void compute_pair_step(const StepRegs& r, const uint3
     const float r0 = fmaf((float)hi[0], mone, w[T][j0]);
     const float r1 = fmaf((float)hi[1], mone, w[T][j0 + 1]);
     const h2_t lo = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
-    // lanes 4-7 and 12-15 of each row take the lo part from lane - 4
-    const uint32_t v = (uint32_t)__builtin_amdgcn_update_dpp(
-        (int)__builtin_bit_cast(uint32_t, hi), (int)__builtin_bit_cast(uint32_t, lo), 0x114, 0xF,
-        0xA, false);
-    A[e] = head_ok ? v : 0u;
+    if constexpr (QS == 8) {
+      A[e] = head_ok ? __builtin_bit_cast(uint32_t, hi) : 0u;
+      Alo[e] = head_ok ? __builtin_bit_cast(uint32_t, lo) : 0u;
+    } else {
+      // lanes 4-7 and 12-15 of each row take the lo part from lane - 4
+      const uint32_t v = (uint32_t)__builtin_amdgcn_update_dpp(
+          (int)__builtin_bit_cast(uint32_t, hi), (int)__builtin_bit_cast(uint32_t, lo), 0x114,
+          0xF, 0xA, false);
+      A[e] = head_ok ? v : 0u;
+    }
   }
 
 #pragma unroll
@@ -926,18 +970,21 @@ __device__ __forceinline__ void compute_pair_step(const StepRegs& r, const uint3
     }
     a.o[2 * beta] = mfma(A, blo, a.o[2 * beta]);
     a.o[2 * beta + 1] = mfma(A, bhi, a.o[2 * beta + 1]);
+    if constexpr (QS == 8) {
+      a.o[2 * beta] = mfma(Alo, blo, a.o[2 * beta]);
+      a.o[2 * beta + 1] = mfma(Alo, bhi, a.o[2 * beta + 1]);
+    }
   }
 }
 
-// GR: query heads per KV head (1, 2 or 4). The wave computes 4 query slots
-// per head whatever GR is (see load_query_pair); with GR = 1 or 2 the spare
-// slots repeat a query: the extra arithmetic is hidden behind the loads, and
-// the wave still reads whole lines. (Eight queries per head do not fit this
-// layout; they run the single-head kernel.)
+// GR: query heads per KV head (1, 2, 4 or 8). The wave computes QS = 4 query
+// slots per head for GR <= 4 (see load_query_pair), 8 for GR = 8; with GR = 1
+// or 2 the spare slots repeat a query: the extra arithmetic is hidden behind
+// the loads, and the wave still reads whole lines.
 template <int GR, bool EARLY, bool STREAM>
 __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
-  constexpr int G = 4;
-  static_assert(GR == 1 || GR == 2 || GR == 4, "queries per KV head");
+  constexpr int G = pair_slots<GR>();
+  static_assert(GR == 1 || GR == 2 || GR == 4 || GR == 8, "queries per KV head");
   // STREAM: the call reads a pool several times larger than the last-level
   // cache, so the code loads are nontemporal and the stream does not displace
   // lines that are reused. Each wave reads whole 128-byte lines (two heads'
@@ -1015,13 +1062,13 @@ __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
   // EARLY: the first step's loads are issued before the query is prepared,
   // which then overlaps their latency
   StepRegs cur, nxt;
-  u4_t bq[4];
+  u4_t bq[4], bq_lo[4];
   float cinit, F;
   if constexpr (EARLY) {
     load_pair_step<true, kAux>(p, cur, t_begin, t_end, blk0, pages, h0, ln);
-    prepare_query<G, true>(p.qp, qraw, lane, xs, bq, cinit, F);
+    prepare_query<G, true>(p.qp, qraw, lane, xs, bq, cinit, F, bq_lo);
   } else {
-    prepare_query<G, true>(p.qp, qraw, lane, xs, bq, cinit, F);
+    prepare_query<G, true>(p.qp, qraw, lane, xs, bq, cinit, F, bq_lo);
     load_pair_step<false, kAux>(p, cur, t_begin, t_end, blk0, pages, h0, ln);
   }
   const float F4 = 4.0f * F;
@@ -1042,13 +1089,38 @@ __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
     }
     __builtin_amdgcn_wave_barrier();
     const bool mask = !(cur.ok[0] && t1 <= t_end);
-    compute_pair_step(cur, ks, vs, bq, cinit, F, F4, a, g, n, head_ok, t0, t_end, mask);
+    compute_pair_step<G>(cur, ks, vs, bq, bq_lo, cinit, F, F4, a, g, n, head_ok, t0, t_end, mask);
     cur = nxt;
   }
 
   // ---- chunk partial ----
-  const float l = rows_sum(head_ok && (n & 4) == 0 ? a.l : 0.0f);
-  const float W = rows_sum(head_ok && (n & 4) == 0 ? a.W : 0.0f);
+  const float l = rows_sum(head_ok && (G == 8 || (n & 4) == 0) ? a.l : 0.0f);
+  const float W = rows_sum(head_ok && (G == 8 || (n & 4) == 0) ? a.W : 0.0f);
+  if constexpr (G == 8) {
+    // rows 4g + j of the accumulators and column n of l, W: query 4g + j
+    // resp. n of the pair, query head 8 h0 + that index
+    float Wq[16];
+#pragma unroll
+    for (int qc = 0; qc < 16; ++qc)
+      Wq[qc] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, W), qc));
+    const int64_t head0 = (int64_t)part * p.Hq + (int64_t)h0 * 8;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float Wv = g == 0 ? Wq[j] : g == 1 ? Wq[4 + j] : g == 2 ? Wq[8 + j] : Wq[12 + j];
+      float vals[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        vals[k] = a.o[k][j] * ((k & 1) ? 1048576.0f : 16777216.0f) - 8.0f * Wv;
+      f4_t* dst = reinterpret_cast<f4_t*>(p.part_o + (head0 + 4 * g + j) * kD + 8 * n);
+      dst[0] = f4_t{vals[0], vals[1], vals[2], vals[3]};
+      dst[1] = f4_t{vals[4], vals[5], vals[6], vals[7]};
+    }
+    if (g == 0) {
+      p.part_ml[(head0 + n) * 2] = a.m == -INFINITY ? -INFINITY : a.mref;
+      p.part_ml[(head0 + n) * 2 + 1] = l;
+    }
+    return;
+  }
   f4_t os[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k)
@@ -1346,7 +1418,8 @@ const void* const kChunk[2][4] = {
   {{(void*)&attn_chunk_pair_kernel<GR, false, false>,                                           \
     (void*)&attn_chunk_pair_kernel<GR, false, true>},                                           \
    {(void*)&attn_chunk_pair_kernel<GR, true, false>, (void*)&attn_chunk_pair_kernel<GR, true, true>}}
-const void* const kChunkPair[3][2][2] = {SAWKV_PAIR(1), SAWKV_PAIR(2), SAWKV_PAIR(4)};
+const void* const kChunkPair[4][2][2] = {SAWKV_PAIR(1), SAWKV_PAIR(2), SAWKV_PAIR(4),
+                                          SAWKV_PAIR(8)};
 #undef SAWKV_PAIR
 
 // A grid of at most four rounds of resident chunk waves (3 per SIMD on 256
@@ -1355,6 +1428,15 @@ const void* const kChunkPair[3][2][2] = {SAWKV_PAIR(1), SAWKV_PAIR(2), SAWKV_PAI
 // grids hide it behind other waves, and there the early loads measured
 // slightly slower.
 constexpr int64_t kEarlyIssueBlocks = 4 * 3 * 4 * 256;
+
+// Eight queries per KV head run the head-pair kernel from two rounds of
+// resident waves (3 per SIMD on 256 compute units) up; smaller grids finish
+// sooner with the single-head kernel's twice as many, shorter waves (which
+// read only half of each line). Measured on the 256-sequence decode batch
+// (64 query heads, contexts uniform in [1, 8000]), us per call single-head /
+// head-pair: 256 sequences (8192 pair blocks) 283 / 252, 128 (8192) 152 /
+// 137, 96 (6144) 114 / 110, 64 (4096) 76 / 78, 16 34 / 37, 1 12.5 / 15.4.
+constexpr int64_t kPairEightBlocks = 2 * 3 * 4 * 256;
 
 // The head-pair kernel reads the codes with nontemporal loads when the
 // contexts the call may read (B x max_context tokens, 132 bytes per token and
@@ -1423,14 +1505,14 @@ int attention_impl(const void* q, int64_t q_stride, const void* k_codes, const v
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
-  // an even head count and at most four queries per head: heads are
-  // processed in pairs, so that every wave reads whole 128-byte lines (the
-  // two heads' 64-byte rows of a token). Measured at 256 sequences: 8 query
-  // heads 257 -> 228 us, 16 query heads 263 -> 232 us against the single-head
-  // kernel; for 8 queries per head, two waves per pair (each with half the
-  // queries, meeting in the L2) took 379 us against 285, so that case keeps
-  // the single-head kernel.
-  const bool pair = H % 2 == 0 && G <= 4;
+  // an even head count: heads are processed in pairs, so that every wave
+  // reads whole 128-byte lines (the two heads' 64-byte rows of a token).
+  // Measured at 256 sequences against the single-head kernel: 8 query heads
+  // 257 -> 228 us, 16 query heads 263 -> 232 us. With eight queries per KV
+  // head a head-pair wave holds 16 queries and twice the matrix-core work
+  // per step; it pays once the grid has kPairEightBlocks blocks.
+  const int64_t pair_blocks = ((B * lay.NC + 7) / 8) * 8 * (H / 2);
+  const bool pair = H % 2 == 0 && (G <= 4 || pair_blocks >= kPairEightBlocks);
   const int32_t groups = pair ? H / 2 : H;
 
   sawkv::attn::ChunkParams cp{};

@@ -10,9 +10,12 @@ log2-unit logits' L1 magnitude):
   * 2^-10 |ref|: the final fp16 rounding (half an ulp is <= 2^-11 |ref|).
   * Vmax * 2^-14: the value side. The weights p * s_v enter the matrix cores as
     fp16 hi + lo (relative error <= 2^-22), products with the codes are exact,
-    float32 accumulation rounds once per 32 tokens, and the +8 code bias is
-    removed with a float32 running sum (<= 2^-17 relative over a chunk, times
-    8).
+    float32 accumulation rounds once per matrix-core product of 32 token
+    slots (twice per 16-token step where the hi and the lo weights enter as
+    two products into one accumulator, eight queries per head in head pairs:
+    at most 128 roundings, 2^-17 relative, over a chunk of 1024 tokens), and
+    the +8 code bias is removed with a float32 running sum (<= 2^-17 relative
+    over a chunk, times 8).
   * Vmax * 2^-17 * Bmax: the logits. The query enters as fp16 hi + lo
     (<= 2^-22 relative per channel); the bias constant and five float32
     roundings of sums bounded by 23 * sum |q'| * 8 give an absolute logit
@@ -161,8 +164,9 @@ def test_few_sequences_long_contexts(env, rot, h):
 
 # at most four queries per KV head and an even H run the head-pair kernel
 # (G = 1 and 2 with repeated query slots: (8, 8), (16, 8), (2, 2), (12, 6);
-# G = 4: (8, 2), (16, 4), (24, 6), (64, 16)); eight queries per KV head or an
-# odd H the single-head kernel ((64, 8), (4, 1), (3, 3), (6, 3), (24, 3))
+# G = 4: (8, 2), (16, 4), (24, 6), (64, 16)); an odd H, or eight queries per
+# KV head on a grid this shallow, the single-head kernel ((64, 8), (4, 1),
+# (3, 3), (6, 3), (24, 3))
 @pytest.mark.parametrize("Hq,H", [(8, 8), (16, 8), (64, 8), (4, 1), (2, 2), (12, 6),
                                   (8, 2), (16, 4), (24, 6), (64, 16), (3, 3), (6, 3),
                                   (24, 3)])
@@ -173,6 +177,40 @@ def test_group_sizes(env, Hq, H):
     got = run_gpu(env, x, int(x["context_lens"].max()), 128, O.ROT_KV)
     ref = run_oracle(x, 128, O.ROT_KV)
     check(got, ref, tolerance(x, 128, O.ROT_KV, np.arange(wl.B), ref), f"G={Hq // H}")
+
+
+def widen_tables(x, max_context):
+    """Block tables padded with -1 to ceil(max_context / P) columns (the
+    bound the call checks; pages past a context's end are never read)."""
+    P = x["k_codes"].shape[1]
+    need = -(-max_context // P)
+    bt = x["block_tables"]
+    if bt.shape[1] < need:
+        pad = np.full((bt.shape[0], need - bt.shape[1]), -1, dtype=bt.dtype)
+        bt = np.concatenate([bt, pad], axis=1)
+    return dict(x, block_tables=bt)
+
+
+# Eight queries per KV head over an even head count run the head-pair kernel
+# (16 queries per wave) once the grid, sequences x chunk slots x head pairs
+# with the chunk slots set by max_context, is deep enough. These cases keep
+# the short, masked attn_small contexts (0 to 1300 tokens, so the oracle stays
+# cheap) and pass a large max_context, which deepens the grid: 50000 gives
+# 256-token chunks, ordinary loads, first loads before the query preparation;
+# 2^17 512-token chunks with nontemporal loads; 2^19 1024-token chunks,
+# nontemporal, first loads after the query preparation.
+@pytest.mark.parametrize("max_context,P,rot,h", [
+    (50000, 16, O.ROT_KV, 128), (50000, 16, O.ROT_NONE, 128), (1 << 17, 16, O.ROT_K, 16),
+    (1 << 17, 16, O.ROT_KV, 64), (1 << 17, 32, O.ROT_KV, 32), (1 << 17, 64, O.ROT_K, 128),
+    (1 << 19, 16, O.ROT_KV, 128), (1 << 19, 16, O.ROT_K, 64)])
+def test_eight_queries_per_head_in_pairs(env, max_context, P, rot, h):
+    wl = small(Hq=64, H=8, P=P, wid=90 + P + h)
+    x = widen_tables(W.attn_inputs(wl), max_context)
+    say(f"attn G=8 head pairs max_context={max_context} P={P} rot={ROTS[rot]} h={h}")
+    got = run_gpu(env, x, max_context, h, rot)
+    ref = run_oracle(x, h, rot)
+    check(got, ref, tolerance(x, h, rot, np.arange(wl.B), ref),
+          f"G=8 pairs max_context={max_context} P={P}")
 
 
 @pytest.mark.parametrize("P", [32, 64])
@@ -217,14 +255,18 @@ def test_strided_q_and_custom_scale(env):
               f"sm={sm}")
 
 
-def test_peaked_softmax_outlier_heads(env):
+# (32 query heads: head pairs of four queries; 64 with a deep grid: head
+# pairs of eight, see test_eight_queries_per_head_in_pairs)
+@pytest.mark.parametrize("Hq,max_context", [(32, 1300), (64, 1 << 17)])
+def test_peaked_softmax_outlier_heads(env, Hq, max_context):
     """Scales 20x larger on two heads per tensor make the softmax nearly
     one-hot there; sharpen further with a large sm_scale."""
-    x = W.attn_inputs(small())
-    say("attn sm_scale=1.0 (peaked)")
-    got = run_gpu(env, x, 1300, 128, O.ROT_K, sm_scale=1.0)
+    x = widen_tables(W.attn_inputs(small(Hq=Hq)), max_context)
+    say(f"attn sm_scale=1.0 (peaked) Hq={Hq} max_context={max_context}")
+    got = run_gpu(env, x, max_context, 128, O.ROT_K, sm_scale=1.0)
     ref = run_oracle(x, 128, O.ROT_K, sm_scale=1.0)
-    check(got, ref, tolerance(x, 128, O.ROT_K, np.arange(9), ref, sm_scale=1.0), "peaked")
+    check(got, ref, tolerance(x, 128, O.ROT_K, np.arange(9), ref, sm_scale=1.0),
+          f"peaked Hq={Hq}")
 
 
 # --------------------------------------------------------------------------
@@ -309,11 +351,10 @@ def test_long_contexts_sampled(env):
 @pytest.mark.parametrize("Hq", [8, 64])
 def test_full_size_other_groupings_sampled(env, Hq):
     """The full 256-sequence pool read by one query head per KV head (G = 1,
-    head pairs with repeated query slots) and by eight (G = 8, single-head
-    kernel), on a grid deeper than four rounds of resident waves (first loads
-    after the query preparation), sampled against the oracle; then the first
-    64 sequences (a shallow grid, first loads issued before the query
-    preparation)."""
+    head pairs with repeated query slots) and by eight (G = 8, head pairs of
+    16 queries), sampled against the oracle; then the first 64 sequences (a
+    shallow grid: first loads issued before the query preparation, and G = 8
+    on the single-head kernel)."""
     wl = dataclasses.replace(W.ATTN_WORKLOADS["attn"], Hq=Hq)
     x = W.attn_inputs(wl)
     L = x["context_lens"]
