@@ -31,7 +31,9 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
  *     never allocates, frees or synchronises, keeps no state between calls
- *     and is safe to call from several host threads.
+ *     and is safe to call from several host threads. (The one exception,
+ *     sawkv_decode_attention_noalloc at the end of this header, keeps its
+ *     partial results in a static device array of the library.)
  *   - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream)
  *     and return. Faults in device memory surface at the caller's next
  *     synchronisation.
