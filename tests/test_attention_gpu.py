@@ -349,6 +349,22 @@ def test_long_contexts_sampled(env):
 
 
 @pytest.mark.parametrize("Hq", [8, 64])
+def test_long_contexts_other_groupings_sampled(env, Hq):
+    """The 64 x 32768-token pool read by one and by eight query heads per KV
+    head (head pairs with repeated query slots, resp. head pairs of 16
+    queries), three sequences against the oracle, every output finite."""
+    wl = dataclasses.replace(W.ATTN_WORKLOADS["attn_long"], Hq=Hq)
+    x = W.attn_inputs(wl)
+    maxc = int(x["context_lens"].max())
+    say(f"attn long contexts Hq={Hq} B={wl.B} L={maxc} P={wl.P}")
+    got = run_gpu(env, x, maxc, wl.h, wl.rot_mode)
+    seqs = np.array([0, 31, 63])
+    ref = run_oracle(x, wl.h, wl.rot_mode, seqs=seqs)
+    check(got[seqs], ref, tolerance(x, wl.h, wl.rot_mode, seqs, ref), f"long Hq={Hq} sampled")
+    assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("Hq", [8, 64])
 def test_full_size_other_groupings_sampled(env, Hq):
     """The full 256-sequence pool read by one query head per KV head (G = 1,
     head pairs with repeated query slots) and by eight (G = 8, head pairs of
