@@ -11,7 +11,9 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sawkv.h")
-LIB = os.path.join(ROOT, "int4_kv_cache_amd", "libsawkv.so")
+# SAWKV_TEST_LIB: another build of the library to check (the host-only
+# AddressSanitizer build of tests/test_host_asan.py)
+LIB = os.environ.get("SAWKV_TEST_LIB") or os.path.join(ROOT, "int4_kv_cache_amd", "libsawkv.so")
 
 OK, EINVAL, EUNSUPPORTED, EALIGN, EHIP = 0, 1, 2, 3, 4
 
