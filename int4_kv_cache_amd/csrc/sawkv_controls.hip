@@ -168,21 +168,34 @@ __device__ __forceinline__ void gather8_tensor(const Gather8Tensor& G, const Gat
 #pragma unroll
     for (int k = 0; k < kElems; ++k) o[k] = x[k] * sf;   // exact
   }
-  if (live) {
-    uint4* dst = reinterpret_cast<uint4*>(G.out + (int64_t)v * kD + 8 * lam);
+  // stage the wave's 16 output rows (4 KB, consecutive vectors) through LDS,
+  // then store them as four contiguous 1 KB wave stores; rows padded to 272
+  // bytes
+  __shared__ uint4 stage[kWaves][kVecPerWave][17];
+  const int wv = threadIdx.x >> 6, vq = (threadIdx.x & 63) >> 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t wd[4];
+  for (int i = 0; i < 4; ++i) {
+    uint32_t wd[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint16_t lo = __builtin_bit_cast(uint16_t, __float2half_rn(opaque(o[8 * i + 2 * k])));
-        const uint16_t hi =
-            __builtin_bit_cast(uint16_t, __float2half_rn(opaque(o[8 * i + 2 * k + 1])));
-        wd[k] = (uint32_t)lo | ((uint32_t)hi << 16);
-      }
-      dst[4 * i] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    for (int k = 0; k < 4; ++k) {
+      const uint16_t lo = __builtin_bit_cast(uint16_t, __float2half_rn(opaque(o[8 * i + 2 * k])));
+      const uint16_t hi =
+          __builtin_bit_cast(uint16_t, __float2half_rn(opaque(o[8 * i + 2 * k + 1])));
+      wd[k] = (uint32_t)lo | ((uint32_t)hi << 16);
     }
+    stage[wv][vq][4 * i + lam] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
   }
+  __builtin_amdgcn_wave_barrier();
+  const int ln = threadIdx.x & 63;
+  const uint32_t v_first = blockIdx.x * (uint32_t)kVecPerBlock + (uint32_t)wv * kVecPerWave;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * i + (ln >> 4), c = ln & 15;
+    const uint4 w = stage[wv][r][c];
+    if (v_first + (uint32_t)r < (uint32_t)p.TH)
+      store_stream(w, G.out + ((int64_t)v_first + r) * kD + 8 * c);
+  }
+  __builtin_amdgcn_wave_barrier();
 }
 
 template <int HB0, int HB1>
