@@ -75,3 +75,38 @@ def test_noalloc_rejects_sizes_beyond_the_scratch(env):
     with pytest.raises(S.SawkvError) as e:
         S.decode_attention_noalloc(d["q"], pools, bt, d["context_lens"], big, h=wl.h)
     assert e.value.status == S.EUNSUPPORTED
+
+
+def test_noalloc_replays_under_graph_capture(env):
+    """The callers it is for: the no-alloc call captured into a HIP graph
+    (after one eager call, which looks up the scratch address). Every replay,
+    with fresh queries written in place beforehand and eager calls of both
+    entry points in between, equals those eager calls byte for byte."""
+    torch, S = env
+    wl = W.ATTN_WORKLOADS["attn_small"]
+    x = W.attn_inputs(wl)
+    d = _dev(torch, x)
+    pools = (d["k_codes"], d["v_codes"], d["k_scales"], d["v_scales"])
+    maxc = int(x["context_lens"].max())
+    q = d["q"].clone()
+    out = torch.empty_like(q)
+    args = (pools, d["block_tables"], d["context_lens"], maxc)
+    S.decode_attention_noalloc(q, *args, h=wl.h, rot="kv", out=out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        S.decode_attention_noalloc(q, *args, h=wl.h, rot="kv", out=out)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    for i in range(4):
+        fresh = rng.standard_normal(tuple(q.shape)).astype(np.float16)
+        q.copy_(torch.from_numpy(fresh).cuda())
+        torch.cuda.synchronize()
+        say(f"graph replay {i}")
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        eager = S.decode_attention_noalloc(q, *args, h=wl.h, rot="kv").cpu().numpy()
+        ref = S.decode_attention(q, *args, h=wl.h, rot="kv").cpu().numpy()
+        assert got.tobytes() == eager.tobytes(), f"replay {i} vs eager no-alloc call"
+        assert got.tobytes() == ref.tobytes(), f"replay {i} vs workspace call"
