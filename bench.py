@@ -532,13 +532,80 @@ def bench_attention(args):
     print(json.dumps(out), flush=True)
 
 
+def measured_step(torch, S, c, app, layer_pools, d, maxc, wa, ws, layers, n):
+    """One whole decode step at concurrency c per rotation mode, captured into
+    a HIP graph and replayed: the layered append, then each layer's attention
+    over its own pool copy (one shared workspace; the calls run in order on
+    one stream). The graph's last output is checked against an eager run of
+    the same step after every timing round."""
+    stream = torch.cuda.current_stream()
+    q, bt, cl = d["q"][:c], d["block_tables"][:c], d["context_lens"][:c]
+    out = {r: torch.empty_like(q) for r in ("k", "none")}
+    att = {r: [S.AttentionCall(q, lp, bt, cl, maxc, h=wa.h, rot=r, out=out[r], workspace=ws)
+               for lp in layer_pools] for r in ("k", "none")}
+
+    def step(r):
+        app[r]()
+        for a in att[r]:
+            a()
+
+    graphs = {}
+    for r in ("k", "none"):
+        step(r)                                   # eager, outside the capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(r)
+        torch.cuda.synchronize()
+        graphs[r] = g
+
+    def check(r):
+        graphs[r].replay()
+        torch.cuda.synchronize()
+        got = out[r].clone()
+        step(r)
+        torch.cuda.synchronize()
+        if not torch.equal(got, out[r]):
+            raise RuntimeError(f"graph replay of the decode step differs from eager ({r})")
+
+    def timed(r):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            graphs[r].replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for r in ("k", "none"):
+        for _ in range(3):
+            graphs[r].replay()
+        check(r)
+    rot, naive = [], []
+    for _ in range(9):
+        naive.append(timed("none"))
+        rot.append(timed("k"))
+        check("k")
+        check("none")
+    return {"rot_us": round(float(np.median(rot)) * 1e3, 2),
+            "naive_us": round(float(np.median(naive)) * 1e3, 2),
+            "rot_over_naive": round(float(np.median(rot) / np.median(naive)), 4),
+            "rot_over_naive_ci95": bootstrap_ratio_ci(rot, naive),
+            "launches_per_step": 1 + 2 * layers, "replays_per_round": n, "rounds": 9}
+
+
 def bench_concurrency(args):
     """The pages' serving claim, measured on this path: rotated INT4 against
     plain (naive) INT4 across concurrency levels. Per decode step at
     concurrency c: the 36 layers' appends of c new tokens in one launch
     (decode recipe, K-only rotation), and decode attention of the c sequences
     over their cached contexts (attn recipe, first c sequences), timed on one
-    layer's pool; the step estimate is append + 36 x attention."""
+    layer's pool; the step estimate is append + 36 x attention. The whole step
+    is also measured: the append launch and 36 attention calls, each layer
+    reading its own copy of the pool (so the layers do not share cached
+    lines), captured into one HIP graph per rotation mode and replayed back
+    to back (its output checked against the same step run eagerly)."""
     import torch
     from int4_kv_cache_amd import sawkv as S
 
@@ -558,6 +625,10 @@ def bench_concurrency(args):
     x = W.attn_inputs(wa)
     d = {k_: torch.from_numpy(np.ascontiguousarray(v_)).to(dev) for k_, v_ in x.items()}
     apools = (d["k_codes"], d["v_codes"], d["k_scales"], d["v_scales"])
+    # one pool copy per layer for the measured step (36 x 1.1 GB)
+    layer_pools = [apools] + [tuple(t.clone() for t in apools) for _ in range(layers - 1)]
+    ws = torch.empty(S.attention_workspace_size(wa.B, wa.Hq, wa.H, int(x["context_lens"].max())),
+                     dtype=torch.uint8, device=dev)
 
     def timed(fn, n):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -598,12 +669,17 @@ def bench_concurrency(args):
                          "rot_over_naive_ci95": bootstrap_ratio_ci(rot, naive)}
         step_rot = res["append"]["rot_us"] + layers * res["attention"]["rot_us"]
         step_naive = res["append"]["naive_us"] + layers * res["attention"]["naive_us"]
+        measured = measured_step(torch, S, c, app, layer_pools, d, maxc, wa, ws, layers,
+                                 max(10, args.steps // 100))
         levels.append({"concurrency": c, "context_tokens": int(L.sum()),
                        "append_36_layers": res["append"], "attention_one_layer": res["attention"],
                        "step_estimate_us": {"rot": round(step_rot, 2), "naive": round(step_naive, 2),
                                             "rot_over_naive": round(step_rot / step_naive, 4)},
-                       "tokens_per_s": round(c / (step_rot * 1e-6), 1)})
-        print(f"[bench] concurrency {c}: step {step_rot:.1f} us (naive {step_naive:.1f})",
+                       "step_measured_us": measured,
+                       "tokens_per_s": round(c / (measured["rot_us"] * 1e-6), 1),
+                       "tokens_per_s_estimate": round(c / (step_rot * 1e-6), 1)})
+        print(f"[bench] concurrency {c}: step {measured['rot_us']:.1f} us measured "
+              f"(naive {measured['naive_us']:.1f}; estimate {step_rot:.1f} / {step_naive:.1f})",
               file=sys.stderr, flush=True)
     wall = time.perf_counter() - t_start
     top = levels[-1]
@@ -615,7 +691,7 @@ def bench_concurrency(args):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": 20,
-        "ms_per_step": round(top["step_estimate_us"]["rot"] * 1e-3, 5),
+        "ms_per_step": round(top["step_measured_us"]["rot_us"] * 1e-3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -624,6 +700,8 @@ def bench_concurrency(args):
         "config": {"workload": ("concurrency sweep: decode recipe (8 KV heads x 128, 36 layers, "
                                 "K-only rotation h=128) for the appends, attn recipe (32 query "
                                 "heads, contexts uniform in [1, 8000], page 16) for attention; "
+                                "step = the 36-layer append launch + 36 attention calls, one "
+                                "pool copy per layer, replayed from a HIP graph (value); "
                                 "step estimate = 36-layer append + 36 x one layer's attention"),
                    "levels": [l["concurrency"] for l in levels], "parallelism": "single GPU"},
         "levels": levels,
