@@ -1360,7 +1360,13 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 Layout make_layout(int64_t B, int32_t Hq, int32_t H, int64_t max_context) {
   Layout L{};
   int C = B * H * ((max_context + 1023) / 1024) >= 16384 ? 1024 : 512;
-  while (C > 128 && B * H * ((max_context + C - 1) / C) < 8192) C >>= 1;
+  // halve while the step would have fewer than `enough` items; eight queries
+  // per KV head run the single-head kernel on such grids, whose waves carry
+  // twice the arithmetic of a head pair's per token and prefer longer chunks
+  // (64 query heads, µs at 16 / 24 / 48 sequences: 29.8 / 40.2 / 64.2 with
+  // 4096 against 33.9 / 46.2 / 69.3 with 8192; 32 query heads lose with 4096)
+  const int64_t enough = Hq / H == 8 ? 4096 : 8192;
+  while (C > 128 && B * H * ((max_context + C - 1) / C) < enough) C >>= 1;
   // a grid that cannot fill the chip even at 128 tokens (one or two long
   // sequences): halve once more, fewer serial steps per wave
   if (C == 128 && B * H * ((max_context + 127) / 128) < 1024) C = 64;
