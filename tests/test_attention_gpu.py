@@ -196,9 +196,8 @@ def widen_tables(x, max_context):
 # with the chunk slots set by max_context, is deep enough. These cases keep
 # the short, masked attn_small contexts (0 to 1300 tokens, so the oracle stays
 # cheap) and pass a large max_context, which deepens the grid: 50000 gives
-# 256-token chunks, ordinary loads, first loads before the query preparation;
-# 2^17 512-token chunks with nontemporal loads; 2^19 1024-token chunks,
-# nontemporal, first loads after the query preparation.
+# 256-token chunks, first loads before the query preparation; 2^17 512-token
+# chunks; 2^19 1024-token chunks, first loads after the query preparation.
 @pytest.mark.parametrize("max_context,P,rot,h", [
     (50000, 16, O.ROT_KV, 128), (50000, 16, O.ROT_NONE, 128), (1 << 17, 16, O.ROT_K, 16),
     (1 << 17, 16, O.ROT_KV, 64), (1 << 17, 32, O.ROT_KV, 32), (1 << 17, 64, O.ROT_K, 128),
@@ -314,8 +313,7 @@ def test_append_then_attention(env):
 # full size: 256 sequences, contexts up to 8000, sampled against the oracle
 # --------------------------------------------------------------------------
 
-# 256 sequences: a deep grid with nontemporal code loads; 128: a shallow grid
-# (first loads before the query preparation) whose pool is still streamed
+# 256 sequences: 1024-token chunks; 128: 512-token chunks
 @pytest.mark.parametrize("B", [256, 128])
 def test_full_size_sampled(env, B):
     wl = W.ATTN_WORKLOADS["attn"]
