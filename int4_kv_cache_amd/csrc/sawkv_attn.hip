@@ -196,6 +196,41 @@ __device__ __forceinline__ float lane_xor(float v, int m) {
   return __builtin_bit_cast(float, r);
 }
 
+// a[k] = a[k] + sg * (a[k] of lane ^ 4) for k < 8, within rows of 16 lanes:
+// the half-row mirror (lane ^ 7) into copies, then the quad reversal
+// (lane ^ 3) inside the multiply-add. One asm block: its first s_nop covers
+// the VALU-write -> DPP-read hazard on a (written before the block), the
+// second on the copies, the last on a for whatever DPP-reads it next (the
+// compiler does not see the block's writes as vector ALU writes).
+__device__ __forceinline__ void xbfly8_lane4(float& a0, float& a1, float& a2, float& a3,
+                                             float& a4, float& a5, float& a6, float& a7,
+                                             float sg) {
+  float t0, t1, t2, t3, t4, t5, t6, t7;
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_mov_b32_dpp %8, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_mov_b32_dpp %9, %1 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_mov_b32_dpp %10, %2 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_mov_b32_dpp %11, %3 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_mov_b32_dpp %12, %4 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_mov_b32_dpp %13, %5 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_mov_b32_dpp %14, %6 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_mov_b32_dpp %15, %7 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %8, %16 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %9, %16 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %10, %16 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %11, %16 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %4, %12, %16 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %5, %13, %16 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %6, %14, %16 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %7, %15, %16 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1"
+      : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(a4), "+v"(a5), "+v"(a6), "+v"(a7),
+        "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5), "=&v"(t6), "=&v"(t7)
+      : "v"(sg));
+}
+
 // The fp16 query channels of the calling lane, as loaded (CPL / 2 words).
 template <int G, bool PAIR>
 struct QueryRaw {
@@ -292,6 +327,7 @@ __device__ __forceinline__ void prepare_query(const QueryParams& p, const QueryR
     x[2 * m] = __low2float(hv);
     x[2 * m + 1] = __high2float(hv);
   }
+  float sgn = 1.0f;              // the lane's sign after the fused stages
   if (p.rot_k) {
 #pragma unroll
     for (int s = 1; s < CPL; s <<= 1) {
@@ -311,15 +347,36 @@ __device__ __forceinline__ void prepare_query(const QueryParams& p, const QueryR
       if (s < p.h) {
         const int m = s / CPL;
         const float sg = (j & m) ? -1.0f : 1.0f;
+        if (CPL % 8 == 0 && (m == 1 || m == 2 || m == 4)) {
+          // x + sg * partner, one v_fmac_f32_dpp per value: that is sg times
+          // f32(sg * x + partner) (rounding is symmetric), so the lane keeps
+          // the sign sg and the next stages (whose partners share it) and
+          // the scaling below absorb it exactly
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-          const float xp = lane_xor(x[e], m);
-          x[e] = __builtin_fmaf(x[e], sg, xp);
+          for (int e = 0; e < CPL; e += 8) {
+            if (m == 1) {
+              xbfly8_lane1(x[e], x[e + 1], x[e + 2], x[e + 3], x[e + 4], x[e + 5], x[e + 6],
+                           x[e + 7], sg);
+            } else if (m == 2) {
+              xbfly8_lane2(x[e], x[e + 1], x[e + 2], x[e + 3], x[e + 4], x[e + 5], x[e + 6],
+                           x[e + 7], sg);
+            } else {
+              xbfly8_lane4(x[e], x[e + 1], x[e + 2], x[e + 3], x[e + 4], x[e + 5], x[e + 6],
+                           x[e + 7], sg);
+            }
+          }
+          sgn *= sg;
+        } else {
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) {
+            const float xp = lane_xor(x[e], m);
+            x[e] = __builtin_fmaf(x[e], sg, xp);
+          }
         }
       }
     }
   }
-  const float mul = p.rot_k ? p.c_h : 1.0f;
+  const float mul = p.rot_k ? p.c_h * sgn : 1.0f;
 
   float v[CPL];
   float amax = 0.0f;
