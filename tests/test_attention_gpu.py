@@ -212,6 +212,20 @@ def test_eight_queries_per_head_in_pairs(env, max_context, P, rot, h):
           f"G=8 pairs max_context={max_context} P={P}")
 
 
+# an odd head count runs the single-head kernel; with four queries per KV
+# head its query rotation spans 16 lanes of 8 channels (three fused cross-lane
+# stages, then one more), every block size h
+@pytest.mark.parametrize("Hq,H", [(4, 1), (12, 3)])
+@pytest.mark.parametrize("h", [16, 32, 64])
+def test_single_head_kernel_block_sizes(env, Hq, H, h):
+    wl = small(Hq=Hq, H=H, h=h, rot_mode=O.ROT_KV, wid=70 + Hq + h)
+    x = W.attn_inputs(wl)
+    say(f"attn single-head G={Hq // H} H={H} h={h}")
+    got = run_gpu(env, x, int(x["context_lens"].max()), h, O.ROT_KV)
+    ref = run_oracle(x, h, O.ROT_KV)
+    check(got, ref, tolerance(x, h, O.ROT_KV, np.arange(wl.B), ref), f"single-head H={H} h={h}")
+
+
 @pytest.mark.parametrize("P", [32, 64])
 def test_page_sizes(env, P):
     wl = small(P=P, wid=20 + P)
