@@ -138,6 +138,15 @@ def _on_gpu(*tensors):
         raise ValueError(f"tensors are on different devices: {sorted(map(str, devs))}")
 
 
+def _slots(slot_mapping, T=None):
+    """slot_mapping must be a contiguous int64 vector (of T entries when T is
+    given): the library reads it as a packed array."""
+    if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1 \
+            or not slot_mapping.is_contiguous() or (T is not None and slot_mapping.numel() != T):
+        raise ValueError("slot_mapping must be a contiguous int64 [T]")
+    return slot_mapping.numel()
+
+
 def _pools_for(H, D, pairs):
     """Geometry (N_pg, P, H, D/2) shared by every present (codes, scales) pair;
     each pool's heads and row width must be those of the K/V rows it holds."""
@@ -192,8 +201,7 @@ def _append_args(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, h, ro
     T, H, D, ks_, vs_ = _kv_pair(k, v)
     pairs = _present_pools(k, v, k_codes, v_codes, k_scales, v_scales)
     N_pg, P = _pools_for(H, D, pairs)[:2]
-    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T:
-        raise ValueError("slot_mapping must be int64 [T]")
+    _slots(slot_mapping, T)
     _on_gpu(k, v, slot_mapping, *[t for pair in pairs for t in pair])
     return (_addr(k), _addr(v), ks_, vs_, _addr(slot_mapping), T, H, D,
             _addr(k_codes) if k is not None else None, _addr(v_codes) if v is not None else None,
@@ -298,8 +306,7 @@ def _layers_args(kv, slot_mapping, pools, h, rot):
     k0, v0 = kv[0]
     T, H, D, ks_, vs_ = _kv_pair(k0, v0)
     pool = _pools_for(H, D, _present_pools(k0, v0, *pools[0]))
-    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T:
-        raise ValueError("slot_mapping must be int64 [T]")
+    _slots(slot_mapping, T)
     descs = (LayerDesc * n)()
     for i, ((k, v), (kc, vc, kss, vss)) in enumerate(zip(kv, pools)):
         # the C call takes one geometry for all layers: insist on it here
@@ -346,9 +353,7 @@ def _gather_args(k_codes, v_codes, k_scales, v_scales, slot_mapping, k_out, v_ou
     H, half = _pool_geometry(*pairs[0])[2:]
     N_pg, P, H, half = _pools_for(H, 2 * half, pairs)
     D = 2 * half
-    T = slot_mapping.numel()
-    if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1:
-        raise ValueError("slot_mapping must be int64 [T]")
+    T = _slots(slot_mapping)
     _on_gpu(slot_mapping, k_out, v_out, *[t for pair in pairs for t in pair])
     dev = (k_codes if want_k else v_codes).device
     if want_k and k_out is None:
@@ -403,7 +408,6 @@ def _attention_common(q, pools, block_tables, context_lens, max_context, h, rot,
     if tuple(_pool_geometry(v_codes, v_scales)) != (N_pg, P, H, half):
         raise ValueError("K and V pools must have the same shape")
     D = 2 * half
-    _on_gpu(q, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens, out)
     if q.dtype != torch.float16 or q.dim() != 3 or q.shape[2] != D or q.stride(2) != 1 \
             or (q.shape[1] > 1 and q.stride(1) != D):
         raise ValueError("q must be fp16 [B, Hq, D] with unit channel stride and head stride D")
@@ -411,6 +415,9 @@ def _attention_common(q, pools, block_tables, context_lens, max_context, h, rot,
     if block_tables.dtype != torch.int32 or block_tables.dim() != 2 \
             or block_tables.shape[0] != B or block_tables.stride(1) != 1:
         raise ValueError("block_tables must be int32 [B, max_pages] with unit column stride")
+    if B > 0 and block_tables.shape[1] < -(-max_context // P):
+        raise ValueError(f"block_tables has {block_tables.shape[1]} columns, fewer than "
+                         f"ceil(max_context / P) = {-(-max_context // P)}")
     if context_lens.dtype != torch.int32 or context_lens.numel() != B \
             or not context_lens.is_contiguous():
         raise ValueError("context_lens must be contiguous int32 [B]")
@@ -418,6 +425,7 @@ def _attention_common(q, pools, block_tables, context_lens, max_context, h, rot,
         out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
     if out.dtype != torch.float16 or tuple(out.shape) != (B, Hq, D) or not out.is_contiguous():
         raise ValueError("out must be contiguous fp16 [B, Hq, D]")
+    _on_gpu(q, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens, out)
     need = attention_workspace_size(B, Hq, H, max_context, D)
     if sm_scale is None:
         sm_scale = 1.0 / float(D) ** 0.5
@@ -533,8 +541,7 @@ def cache_append(k, v, slot_mapping, k_cache, v_cache, *, stream=None):
     cache = k_cache if k is not None else v_cache
     if k is not None and v is not None and tuple(k_cache.shape) != tuple(v_cache.shape):
         raise ValueError("K and V caches differ in shape")
-    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T:
-        raise ValueError("slot_mapping must be int64 [T]")
+    _slots(slot_mapping, T)
     _on_gpu(k, v, slot_mapping, k_cache if k is not None else None,
             v_cache if v is not None else None)
     _check(lib.sawkv_cache_append(_addr(k), _addr(v), strides[0], strides[1],
@@ -550,8 +557,7 @@ def int8_append(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, *, h=1
     T, H, D, ks_, vs_ = _kv_pair(k, v)
     pairs = _present_pools(k, v, k_codes, v_codes, k_scales, v_scales)
     pool = _int8_pools_for(H, D, pairs)
-    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T:
-        raise ValueError("slot_mapping must be int64 [T]")
+    _slots(slot_mapping, T)
     _on_gpu(k, v, slot_mapping, *[t for pair in pairs for t in pair])
     _check(lib.sawkv_int8_append(
         _addr(k), _addr(v), ks_, vs_, _addr(slot_mapping), T, H, D,
@@ -569,9 +575,7 @@ def int8_gather(k_codes, v_codes, k_scales, v_scales, slot_mapping, *, h=128, ro
              if want]
     H, D = _int8_pool_geometry(*pairs[0])[2:]
     N_pg, P, H, D = _int8_pools_for(H, D, pairs)
-    T = slot_mapping.numel()
-    if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1:
-        raise ValueError("slot_mapping must be int64 [T]")
+    T = _slots(slot_mapping)
     _on_gpu(slot_mapping, k_out, v_out, *[t for pair in pairs for t in pair])
     dev = (k_codes if want_k else v_codes).device
     if want_k and k_out is None:

@@ -98,3 +98,50 @@ def test_attention_cpu_tensors_are_refused(S):
     cl = torch.zeros((2,), dtype=torch.int32)
     with pytest.raises(ValueError, match="GPU"):
         S.decode_attention(q, pools(S), bt, cl, 64)
+
+
+def test_strided_slot_mapping_is_refused(S):
+    # the library reads slot_mapping as a packed int64 array: a strided view
+    # would hand it other tensors' values
+    k, v, _ = kv()
+    s = torch.zeros((32,), dtype=torch.int64)[::2]
+    with pytest.raises(ValueError, match="contiguous int64"):
+        S.quantize_append(k, v, s, *pools(S))
+    with pytest.raises(ValueError, match="contiguous int64"):
+        S.naive_int4_append(k, v, s, *pools(S))
+    with pytest.raises(ValueError, match="contiguous int64"):
+        S.dequant_gather(*pools(S), s)
+    with pytest.raises(ValueError, match="contiguous int64"):
+        S.quantize_append_layers([(k, v)], s, [pools(S)])
+    with pytest.raises(ValueError, match="contiguous int64"):
+        S.int8_append(k, v, s, *S.alloc_int8_pools(4, 16, 8, 128, "cpu"))
+    with pytest.raises(ValueError, match="contiguous int64"):
+        S.int8_gather(*S.alloc_int8_pools(4, 16, 8, 128, "cpu"), s)
+    with pytest.raises(ValueError, match="contiguous int64"):
+        S.cache_append(k, v, s, torch.zeros((4, 16, 8, 128), dtype=torch.float16),
+                       torch.zeros((4, 16, 8, 128), dtype=torch.float16))
+
+
+def test_slot_mapping_of_other_length_or_type_is_refused(S):
+    k, v, _ = kv(T=16)
+    with pytest.raises(ValueError, match="contiguous int64"):
+        S.quantize_append(k, v, torch.zeros((15,), dtype=torch.int64), *pools(S))
+    with pytest.raises(ValueError, match="contiguous int64"):
+        S.quantize_append(k, v, torch.zeros((16,), dtype=torch.int32), *pools(S))
+
+
+def test_attention_block_table_narrower_than_context_is_refused(S):
+    # max_context 100 with 16-token pages needs 7 page ids per sequence
+    q = torch.zeros((2, 32, 128), dtype=torch.float16)
+    bt = torch.zeros((2, 6), dtype=torch.int32)
+    cl = torch.zeros((2,), dtype=torch.int32)
+    with pytest.raises(ValueError, match="columns"):
+        S.decode_attention(q, pools(S), bt, cl, 100)
+    with pytest.raises(ValueError, match="columns"):
+        S.decode_attention_noalloc(q, pools(S), bt, cl, 100)
+    # a view of a wider table keeps its row stride but not its width
+    wide = torch.zeros((2, 8), dtype=torch.int32)
+    with pytest.raises(ValueError, match="columns"):
+        S.decode_attention(q, pools(S), wide[:, :6], cl, 100)
+    with pytest.raises(ValueError, match="GPU"):
+        S.decode_attention(q, pools(S), wide[:, :7], cl, 100)
