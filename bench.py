@@ -32,11 +32,12 @@ Prints ONE JSON line. Alongside the step it times, on the same batch:
 Roofline: achieved HBM GB/s of the append kernel (algorithmic bytes per launch
 over the event-timed average launch) against the MI355X HBM3E peak, 8 TB/s.
 
-With --workload attn one step is one sawkv_decode_attention call (chunk
-kernel with the query preparation folded in, then the combine) over 256
-sequences whose contexts already sit in the INT4 pool; its bytes are the K and
-V codes and scales of every context token, the queries, the outputs and the
-block tables.
+With --workload attn one step is one sawkv_decode_attention call over 256
+sequences whose contexts already sit in the INT4 pool (at this size the lean
+split: every 16-token step of the batch divided evenly over the resident
+waves, the query preparation folded in; then the merge of the partials); its
+bytes are the K and V codes and scales of every context token, the queries,
+the outputs and the block tables.
 """
 import argparse
 import dataclasses
@@ -505,15 +506,16 @@ def bench_attention(args):
                    "query_heads": wl.Hq, "kv_heads": wl.H, "head_dim": wl.D,
                    "page_size": wl.P, "rotation": ROT_NAME[rot], "block_size_h": h,
                    "parallelism": "single GPU"},
-        "step": ("sawkv_decode_attention: chunk kernel (query prep folded in) + combine "
-                 "(2 launches)"),
+        "step": ("sawkv_decode_attention: split-context kernel (query prep folded in) + "
+                 "merge (2 launches)"),
         "decode_tokens_per_s": round(wl.B / (wall_ms * 1e-3), 1),
         "context_tokens_per_s": round(int(L.sum()) / (wall_ms * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,
-                     "kernel": "one sawkv_decode_attention call (attn_chunk_pair_kernel + "
+                     "kernel": "one sawkv_decode_attention call (attn_lean_pair_kernel, or "
+                               "attn_chunk_pair_kernel below the lean split's sizes, + "
                                "attn_combine_kernel)"},
         "vs_naive": {"rot_ms_median": round(float(np.median(rot_ms)), 5),
                      "naive_ms_median": round(float(np.median(naive_ms)), 5),

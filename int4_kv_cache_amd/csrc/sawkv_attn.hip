@@ -61,6 +61,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 #include <stdio.h>
 
@@ -472,6 +473,10 @@ struct ChunkParams {
   int64_t N_pg;
   int32_t P, H, Hq, NC, C, max_context;
   uint32_t n_groups;       // B * NC
+  // lean form: waves per head pair, sequences, and the merge's view of
+  // each sequence (first wave holding its steps, number of such waves)
+  int32_t lean_waves, lean_seqs;
+  int2* lean_seq;
 };
 
 // Registers of one 32-token step as loaded from memory (tiles T = 0, 1 of 16
@@ -1034,12 +1039,22 @@ __device__ __forceinline__ void compute_pair_step(const StepRegs& r, const uint3
   }
 }
 
+// Tokens [t_begin, t_end) of sequence b for head pair hp, one wave: the
+// partial (reference exponent, denominator, weighted values) of every query
+// of the pair goes to partial row `part`. t_begin is a multiple of 16.
+// WINDOWS: the range may span more than 64 pages; the page ids are then held
+// 64 at a time (one per lane), the next 64 loaded while the current ones are
+// used. Without it the range spans at most 64 pages.
+//
 // GR: query heads per KV head (1, 2, 4 or 8). The wave computes QS = 4 query
 // slots per head for GR <= 4 (see load_query_pair), 8 for GR = 8; with GR = 1
 // or 2 the spare slots repeat a query: the extra arithmetic is hidden behind
 // the loads, and the wave still reads whole lines.
-template <int GR, bool EARLY>
-__global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
+template <int GR, bool EARLY, bool WINDOWS>
+__device__ __forceinline__ void pair_piece(const ChunkParams& p, const int b, const int hp,
+                                           const int t_begin, const int t_end,
+                                           const int64_t part, uint16_t* sstage,
+                                           float (*xs)[kD]) {
   constexpr int G = pair_slots<GR>();
   static_assert(GR == 1 || GR == 2 || GR == 4 || GR == 8, "queries per KV head");
   // The code loads are nontemporal: in a decode step every layer's pool is
@@ -1053,43 +1068,18 @@ __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
   // faster with ordinary loads up to 64 sequences, because it then stays
   // cached between calls.
   constexpr int kAux = 2;
-  __shared__ uint16_t sstage[64];
-  __shared__ float xs[2 * G][kD];
   const int lane = threadIdx.x;
   const int g = lane >> 4, n = lane & 15;
-  const int HP = p.H / 2;
-
-  // Block -> (chunk, sequence, head pair), the pairs of one (sequence, chunk)
-  // on consecutive blocks of one XCD.
-  const uint32_t bx = blockIdx.x;
-  const uint32_t r8 = bx >> 3;
-  const int hp = (int)(r8 % (uint32_t)HP);
-  const uint32_t grp = (r8 / (uint32_t)HP) * 8u + (bx & 7u);
-  if (grp >= p.n_groups) return;
-  // Groups of chunks in dispatch order, counted from the end of each context:
-  // group r holds chunk nck - NC + r of every sequence (nck = its chunk
-  // count), so whole chunks go first and the partial last chunks (r = NC - 1)
-  // last, which keeps the final round of waves short (longest work first).
-  const uint32_t nb = p.n_groups / (uint32_t)p.NC;
-  // the groups of XCD x are those with grp % 8 == x; offsetting the sequence
-  // by r spreads the chunks of one sequence over the XCDs (when nb % 8 == 0
-  // group r of sequence b goes to XCD (b + r) % 8), so every XCD gets a share
-  // of every context, not whole ones
-  const int r = (int)(grp / nb);
-  const int b = (int)((grp % nb + nb - (uint32_t)r % nb) % nb);
-  int L = p.context_lens[b];
-  L = L < 0 ? 0 : (L > p.max_context ? p.max_context : L);
-  const int c = (L + p.C - 1) / p.C - p.NC + r;     // chunk index; < 0: none
-  if (c < 0) return;
-  const uint32_t part = (uint32_t)b * p.NC + c;    // partial slot (b, c)
-  const int t_begin = c * p.C;
-  if (t_begin >= L) return;
-  const int t_end = min(t_begin + p.C, L);
   const int h0 = 2 * hp;
 
-  const int blk0 = t_begin / p.P;
-  const int n_blk = (t_end - 1) / p.P - blk0 + 1;
-  const int pages = lane < n_blk ? p.block_tables[(int64_t)b * p.bt_stride + blk0 + lane] : -1;
+  int blk0 = t_begin / p.P;
+  const int blk_last = (t_end - 1) / p.P;
+  const int32_t* bt_row = p.block_tables + (int64_t)b * p.bt_stride;
+  int pages = lane <= blk_last - blk0 ? bt_row[blk0 + lane] : -1;
+  int pages_next = -1;
+  if constexpr (WINDOWS) {
+    if (blk_last - blk0 >= 64) pages_next = lane <= blk_last - blk0 - 64 ? bt_row[blk0 + 64 + lane] : -1;
+  }
   // the query's load goes out between the page ids and the first step, so
   // each wait takes only what it needs (loads complete in issue order)
   const QueryRaw<G, true> qraw = load_query_pair<GR>(p.qp, b, hp, lane);
@@ -1137,7 +1127,18 @@ __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
   const float F4 = 4.0f * F;
   for (int t0 = t_begin; t0 < t_end; t0 += 16) {
     const int t1 = t0 + 16;
-    if (t1 < t_end) load_pair_step<false, kAux>(p, nxt, t1, t_end, blk0, pages, h0, ln);
+    if (t1 < t_end) {
+      if constexpr (WINDOWS) {
+        // the next step opens the next 64 pages (wave-uniform): their ids
+        // were loaded with the previous window's, the following ones go out now
+        if (t1 / p.P - blk0 >= 64) {
+          blk0 += 64;
+          pages = pages_next;
+          pages_next = lane <= blk_last - blk0 - 64 ? bt_row[blk0 + 64 + lane] : -1;
+        }
+      }
+      load_pair_step<false, kAux>(p, nxt, t1, t_end, blk0, pages, h0, ln);
+    }
     sstage[lane] = (uint16_t)cur.sc;
     __builtin_amdgcn_wave_barrier();
     uint32_t ks[2][2], vs[2][2];
@@ -1156,7 +1157,7 @@ __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
     cur = nxt;
   }
 
-  // ---- chunk partial ----
+  // ---- partial ----
   const float l = rows_sum(head_ok && (G == 8 || (n & 4) == 0) ? a.l : 0.0f);
   const float W = rows_sum(head_ok && (G == 8 || (n & 4) == 0) ? a.W : 0.0f);
   if constexpr (G == 8) {
@@ -1166,7 +1167,7 @@ __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
 #pragma unroll
     for (int qc = 0; qc < 16; ++qc)
       Wq[qc] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, W), qc));
-    const int64_t head0 = (int64_t)part * p.Hq + (int64_t)h0 * 8;
+    const int64_t head0 = part * p.Hq + (int64_t)h0 * 8;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float Wv = g == 0 ? Wq[j] : g == 1 ? Wq[4 + j] : g == 2 ? Wq[8 + j] : Wq[12 + j];
@@ -1200,7 +1201,7 @@ __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
                                                                  8 * (qc >> 2) + (qc & 3)));
   // query slot j of head hh is query head (h0 + hh) GR + j; spare slots
   // (j >= GR) are not written
-  const int64_t head0 = (int64_t)part * p.Hq + (int64_t)h0 * GR;
+  const int64_t head0 = part * p.Hq + (int64_t)h0 * GR;
   if ((g & 1) == 0) {                       // g = 0: head 0, g = 2: head 1
     const int hh = g >> 1;
 #pragma unroll
@@ -1222,6 +1223,160 @@ __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
   }
 }
 
+// One (chunk, sequence, head pair) per block: chunk c covers tokens
+// [c C, (c + 1) C) of the sequence.
+template <int GR, bool EARLY>
+__global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
+  __shared__ uint16_t sstage[64];
+  __shared__ float xs[2 * pair_slots<GR>()][kD];
+  const int HP = p.H / 2;
+
+  // Block -> (chunk, sequence, head pair), the pairs of one (sequence, chunk)
+  // on consecutive blocks of one XCD.
+  const uint32_t bx = blockIdx.x;
+  const uint32_t r8 = bx >> 3;
+  const int hp = (int)(r8 % (uint32_t)HP);
+  const uint32_t grp = (r8 / (uint32_t)HP) * 8u + (bx & 7u);
+  if (grp >= p.n_groups) return;
+  // Groups of chunks in dispatch order, counted from the end of each context:
+  // group r holds chunk nck - NC + r of every sequence (nck = its chunk
+  // count), so whole chunks go first and the partial last chunks (r = NC - 1)
+  // last, which keeps the final round of waves short (longest work first).
+  const uint32_t nb = p.n_groups / (uint32_t)p.NC;
+  // the groups of XCD x are those with grp % 8 == x; offsetting the sequence
+  // by r spreads the chunks of one sequence over the XCDs (when nb % 8 == 0
+  // group r of sequence b goes to XCD (b + r) % 8), so every XCD gets a share
+  // of every context, not whole ones
+  const int r = (int)(grp / nb);
+  const int b = (int)((grp % nb + nb - (uint32_t)r % nb) % nb);
+  int L = p.context_lens[b];
+  L = L < 0 ? 0 : (L > p.max_context ? p.max_context : L);
+  const int c = (L + p.C - 1) / p.C - p.NC + r;     // chunk index; < 0: none
+  if (c < 0) return;
+  const uint32_t part = (uint32_t)b * p.NC + c;    // partial slot (b, c)
+  const int t_begin = c * p.C;
+  if (t_begin >= L) return;
+  const int t_end = min(t_begin + p.C, L);
+  pair_piece<GR, EARLY, false>(p, b, hp, t_begin, t_end, part, sstage, xs);
+}
+
+// Equal work per wave: the 16-token steps of all sequences, in sequence
+// order, are split into n ranges of equal length per head pair (wave k takes
+// steps [k S / n, (k + 1) S / n) of the S steps); a range covers the end of
+// one sequence, whole sequences and the start of another, one partial each,
+// in partial row b + k (distinct for every (sequence, wave) that meet, since
+// both only grow along the steps). Every wave streams from the first step to
+// about the same end, so no round of waves starts or drains while others
+// stream. A wave whose range is empty (fewer steps than waves) writes an
+// empty partial where the merge may look for one.
+//
+// Every wave derives the split itself from the context lengths (at most
+// kLeanMaxB sequences, 16 per lane): S_b = ceil(L_b / 16) steps per sequence
+// (L_b clipped to [0, max_context]), their prefix sums P_b, the sequence and
+// local step where its range starts; and for the merge, for each sequence
+// whose first step P_b lies in its range, the first wave holding its steps
+// (this one) and their number: the wave holding step s is
+// floor(((s + 1) n - 1) / S). Wave 0 marks the empty sequences.
+constexpr int kLeanMaxB = 1024;
+
+template <int GR>
+__global__ __launch_bounds__(64) void attn_lean_pair_kernel(ChunkParams p) {
+  __shared__ uint16_t sstage[64];
+  __shared__ float xs[2 * pair_slots<GR>()][kD];
+  const int HP = p.H / 2;
+  const int lane = threadIdx.x;
+  // block -> (wave k, head pair): the pairs of one range on one XCD
+  const uint32_t bx = blockIdx.x;
+  const uint32_t r8 = bx >> 3;
+  const int hp = (int)(r8 % (uint32_t)HP);
+  const int k = (int)((r8 / (uint32_t)HP) * 8u + (bx & 7u));
+  const int N = p.lean_waves;
+  if (k >= N) return;
+
+  // steps of the lane's sequences 16 lane + j, and their sum
+  int st[16];
+  int lsum = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int bb = 16 * lane + j;
+    int L = bb < p.lean_seqs ? p.context_lens[bb] : 0;
+    L = L < 0 ? 0 : (L > p.max_context ? p.max_context : L);
+    st[j] = (L + 15) >> 4;
+    lsum += st[j];
+  }
+  int incl = lsum;                          // inclusive prefix over the lanes
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d);
+    if (lane >= d) incl += v;
+  }
+  const int excl = incl - lsum;
+  const int64_t S = __builtin_amdgcn_readlane(incl, 63);
+  const int64_t lo = S > 0 ? (int64_t)k * S / N : 0;
+  const int64_t hi = S > 0 ? (int64_t)(k + 1) * S / N : 0;
+  if (hp == 0) {
+    // the merge's view of the lane's sequences
+    int pre = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int bb = 16 * lane + j;
+      const int64_t Pb = (int64_t)excl + pre;
+      if (bb < p.lean_seqs) {
+        if (st[j] == 0) {
+          if (k == 0) p.lean_seq[bb] = make_int2(0, 0);
+        } else if (lo <= Pb && Pb < hi) {
+          const int64_t kl = ((Pb + st[j]) * N - 1) / S;
+          p.lean_seq[bb] = make_int2(k, (int)(kl - k + 1));
+        }
+      }
+      pre += st[j];
+    }
+  }
+  if (S == 0) return;
+  // the sequence holding step lo: its lane, then its place in the lane
+  const uint64_t ball = __ballot(excl <= lo && lo < (int64_t)excl + lsum);
+  const int lam = __ffsll((unsigned long long)ball) - 1;
+  const int off = (int)(lo - __builtin_amdgcn_readlane(excl, lam));
+  int b = -1, s0 = 0, pre = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int sj = __builtin_amdgcn_readlane(st[j], lam);
+    if (b < 0 && off < pre + sj) {
+      b = 16 * lam + j;
+      s0 = off - pre;
+    }
+    pre += sj;
+  }
+  int64_t rem = hi - lo;
+  if (rem == 0) {
+    // an empty partial (no token) for every query of the pair
+    if (lane < 2 * GR) {
+      const int64_t row = ((int64_t)b + k) * p.Hq + (int64_t)2 * hp * GR + lane;
+      p.part_ml[row * 2] = -INFINITY;
+      p.part_ml[row * 2 + 1] = 0.0f;
+    }
+    return;
+  }
+  for (;;) {
+    int L = p.context_lens[b];
+    L = L < 0 ? 0 : (L > p.max_context ? p.max_context : L);
+    const int steps = (L + 15) >> 4;
+    const int nstep = (int)min((int64_t)(steps - s0), rem);
+    const int t_begin = 16 * s0;
+    const int t_end = min(16 * (s0 + nstep), L);
+    pair_piece<GR, true, true>(p, b, hp, t_begin, t_end, (int64_t)b + k, sstage, xs);
+    rem -= nstep;
+    if (rem <= 0) break;
+    // the next sequence with a token (the range ends inside one)
+    for (;;) {
+      ++b;
+      const int Ln = p.context_lens[b];
+      if ((Ln < 0 ? 0 : (Ln > p.max_context ? p.max_context : Ln)) > 0) break;
+    }
+    s0 = 0;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // combine: merge chunks, normalise, un-rotate V, fp16
 // ---------------------------------------------------------------------------
@@ -1233,6 +1388,9 @@ struct CombineParams {
   __half* out;             // [B][Hq][128]
   int64_t n_vec;           // B * Hq
   int32_t Hq, NC, C, max_context;
+  // lean form: per sequence, the first wave holding its steps and the
+  // number of such waves (its partials are rows b + first ...); else null
+  const int2* lean_seq;
 };
 
 // Sum of v over the four quads of a row of 16 lanes (DPP row rotations by 4,
@@ -1275,7 +1433,11 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(CombineParams p) {
     qh = live ? (int)(v % p.Hq) : 0;
   }
   const int L_raw = live ? p.context_lens[b] : 0;
-  const int64_t base = b * p.NC * p.Hq + qh;      // chunk c adds c * Hq
+  // chunk form: chunk c of sequence b in row (b NC + c) Hq + qh; lean form:
+  // the j-th wave holding sequence b in row (b + first + j) Hq + qh
+  const bool lean = p.lean_seq != nullptr;
+  const int2 sk = lean && live ? p.lean_seq[b] : make_int2(0, 0);
+  const int64_t base = (lean ? b + sk.x : b * p.NC) * p.Hq + qh;   // piece c adds c * Hq
 
   // running reference M: a chunk with a larger one rescales what is summed
   float M = -INFINITY;
@@ -1324,7 +1486,7 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(CombineParams p) {
   // are loaded but never merged. The 4-lane form waits for the length and
   // loads only the chunks it merges.
   int nfetch = 0;
-  if constexpr (QPV == 16) {
+  if (QPV == 16 && !lean) {
     nfetch = p.NC > qd ? (p.NC - qd + QPV - 1) / QPV : 0;
 #pragma unroll
     for (int k = 0; k < kDepth - 1; ++k)
@@ -1332,9 +1494,9 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(CombineParams p) {
     __builtin_amdgcn_sched_barrier(0);           // keep the length's wait below these loads
   }
   const int L = L_raw < 0 ? 0 : (L_raw > p.max_context ? p.max_context : L_raw);
-  const int nck = (L + p.C - 1) / p.C;
+  const int nck = lean ? sk.y : (L + p.C - 1) / p.C;
   const int mine = nck > qd ? (nck - qd + QPV - 1) / QPV : 0;
-  if constexpr (QPV == 4) {
+  if (QPV == 4 || lean) {
     nfetch = mine;
 #pragma unroll
     for (int k = 0; k < kDepth - 1; ++k)
@@ -1404,8 +1566,34 @@ constexpr int64_t kMaxContext = INT64_C(1) << 30;
 struct Layout {
   int C;                   // tokens per chunk
   int64_t NC;              // chunks per sequence
-  size_t ml, o, total;     // byte offsets and size
+  size_t ml, o;            // chunk form: byte offsets of the partials
+  // lean form (when the sizes allow it): split plan and partials for at most
+  // lean_waves waves per head pair
+  bool lean;
+  int32_t lean_waves;
+  size_t l_seq, l_ml, l_o;
+  size_t total;            // bytes for either form
 };
+
+// The lean form (equal steps per wave, see attn_lean_pair_kernel) serves
+// steps with many tokens per head pair: at least kLeanMinSteps 16-token steps
+// if every sequence had max_context tokens (fewer than 2^31, counted in 32
+// bits), at most kLeanMaxB sequences (16 per lane of a wave), an even number
+// of KV heads (head pairs). Its grid is the resident waves of the device, at
+// most kLeanMaxWaves.
+// Measured on the decode batch (contexts uniform in [1, 8000], page 16), us
+// per call chunk form / lean form: 256 sequences 232.1 / 220.6 (32 query
+// heads), 251.5 / 238.4 (64), 223.1 / 206.3 (8); 128 sequences 122.9 / 120.6,
+// 139.2 / 131.2, 115.3 / 112.3; 64 sequences (32 000 steps) 69.4 / 72.4,
+// 76.5 / 78.6, 65.7 / 66.1; 64 contexts of 32 768 tokens 409.0 / 398.9.
+constexpr int64_t kLeanMinSteps = 49152;
+constexpr int kLeanMaxWaves = 4096;
+
+bool lean_sizes(int64_t B, int32_t H, int64_t max_context) {
+  const int64_t steps = B * ((max_context + 15) / 16);
+  return H % 2 == 0 && B > 0 && B <= sawkv::attn::kLeanMaxB && steps >= kLeanMinSteps &&
+         steps < (INT64_C(1) << 31);
+}
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -1441,6 +1629,19 @@ Layout make_layout(int64_t B, int32_t Hq, int32_t H, int64_t max_context) {
   L.o = off;
   off = align256(off + (size_t)B * L.NC * Hq * sawkv::kD * 4);
   L.total = off;
+  L.lean = lean_sizes(B, H, max_context);
+  if (L.lean) {
+    L.lean_waves = kLeanMaxWaves / (H / 2);
+    const size_t rows = (size_t)(B + L.lean_waves) * Hq;   // partial rows b + k
+    size_t lo = 0;
+    L.l_seq = lo;
+    lo = align256(lo + (size_t)B * 8);
+    L.l_ml = lo;
+    lo = align256(lo + rows * 2 * 4);
+    L.l_o = lo;
+    lo = align256(lo + rows * sawkv::kD * 4);
+    if (lo > L.total) L.total = lo;
+  }
   return L;
 }
 
@@ -1503,6 +1704,42 @@ constexpr int64_t kEarlyIssueBlocks = 4 * 3 * 4 * 256;
 // head-pair: 256 sequences (8192 pair blocks) 283 / 252, 128 (8192) 152 /
 // 137, 96 (6144) 114 / 110, 64 (4096) 76 / 78, 16 34 / 37, 1 12.5 / 15.4.
 constexpr int64_t kPairEightBlocks = 2 * 3 * 4 * 256;
+
+using sawkv::attn::attn_lean_pair_kernel;
+
+const void* const kLeanPair[4] = {(void*)&attn_lean_pair_kernel<1>, (void*)&attn_lean_pair_kernel<2>,
+                                  (void*)&attn_lean_pair_kernel<4>, (void*)&attn_lean_pair_kernel<8>};
+
+// Lean waves per head pair on the device of `stream`: the waves the device
+// keeps resident at once (occupancy of the lean kernel times compute units,
+// asked once per device and grouping), at most kLeanMaxWaves over all pairs
+// and max_per_pair per pair, a multiple of 8; 0 if the device cannot say.
+constexpr int kLeanDevices = 64;
+std::mutex g_lean_mu;
+int g_lean_resident[kLeanDevices][4] = {};
+
+int lean_waves_per_pair(hipStream_t stream, int gi, int HP, int max_per_pair) {
+  int dev = -1;
+  if ((stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev)) != hipSuccess || dev < 0 ||
+      dev >= kLeanDevices)
+    return 0;
+  int resident;
+  {
+    std::lock_guard<std::mutex> lock(g_lean_mu);
+    resident = g_lean_resident[dev][gi];
+    if (resident == 0) {
+      int per_cu = 0, cus = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kLeanPair[gi], 64, 0) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        per_cu = cus = 0;
+      resident = per_cu > 0 && cus > 0 ? per_cu * cus : -1;
+      g_lean_resident[dev][gi] = resident;
+    }
+  }
+  if (resident <= 0) return 0;
+  const int per_pair = std::min(std::min(resident, kLeanMaxWaves) / HP, max_per_pair);
+  return per_pair / 8 * 8;
+}
 
 const void* const kCombine[2][5] = {
     {(void*)&attn_combine_kernel<0, 4>, (void*)&attn_combine_kernel<16, 4>,
@@ -1597,6 +1834,36 @@ int attention_impl(const void* q, int64_t q_stride, const void* k_codes, const v
   cp.C = lay.C;
   cp.max_context = (int32_t)max_context;
   cp.n_groups = (uint32_t)(B * lay.NC);
+  const int hv = rot_mode == SAWKV_ROT_KV ? (h == 16 ? 1 : h == 32 ? 2 : h == 64 ? 3 : 4) : 0;
+  sawkv::attn::CombineParams mp{};
+  mp.context_lens = context_lens;
+  mp.out = static_cast<__half*>(out);
+  mp.n_vec = B * Hq;
+  mp.Hq = Hq;
+  mp.C = lay.C;
+  mp.max_context = (int32_t)max_context;
+
+  // the lean form: split plan, equal-steps waves, merge
+  const int nwp = lay.lean ? lean_waves_per_pair(s, g_index(G), H / 2, lay.lean_waves) : 0;
+  if (nwp >= 8) {
+    cp.part_o = reinterpret_cast<float*>(ws + lay.l_o);
+    cp.part_ml = reinterpret_cast<float*>(ws + lay.l_ml);
+    cp.lean_waves = nwp;
+    cp.lean_seqs = (int32_t)B;
+    cp.lean_seq = reinterpret_cast<int2*>(ws + lay.l_seq);
+    if ((st = launch64(kLeanPair[g_index(G)], (int64_t)nwp * (H / 2), &cp, s))) return st;
+    mp.part_o = cp.part_o;
+    mp.part_ml = cp.part_ml;
+    mp.lean_seq = cp.lean_seq;
+    mp.NC = 0;
+    // a whole wave per vector when a sequence meets many waves (few
+    // sequences): nwp / B of them on average
+    const bool wide = (int64_t)nwp > 16 * B && B * Hq < 4096;
+    if ((st = launch64(kCombine[wide ? 1 : 0][hv], wide ? B * Hq : (B * Hq + 3) / 4, &mp, s)))
+      return st;
+    return ok();
+  }
+
   const int64_t chunk_blocks = ((B * lay.NC + 7) / 8) * 8 * groups;
   const int early = chunk_blocks <= kEarlyIssueBlocks ? 1 : 0;
   if (max_context > 0 &&
@@ -1605,17 +1872,9 @@ int attention_impl(const void* q, int64_t q_stride, const void* k_codes, const v
                      chunk_blocks, &cp, s)))
     return st;
 
-  sawkv::attn::CombineParams mp{};
   mp.part_o = cp.part_o;
   mp.part_ml = cp.part_ml;
-  mp.context_lens = context_lens;
-  mp.out = static_cast<__half*>(out);
-  mp.n_vec = B * Hq;
-  mp.Hq = Hq;
   mp.NC = cp.NC;
-  mp.C = lay.C;
-  mp.max_context = (int32_t)max_context;
-  const int hv = rot_mode == SAWKV_ROT_KV ? (h == 16 ? 1 : h == 32 ? 2 : h == 64 ? 3 : 4) : 0;
   // more chunks than one round of 4-deep loads per quad, over few vectors: a
   // whole wave per vector (16 quads), so each quad merges a quarter as many
   // chunks; otherwise 4 vectors per wave

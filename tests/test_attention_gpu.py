@@ -324,11 +324,78 @@ def test_append_then_attention(env):
 
 
 # --------------------------------------------------------------------------
+# the lean split: from 49 152 steps of 16 tokens (B * ceil(max_context / 16))
+# up to 1024 sequences with an even KV-head count, the step's 16-token steps
+# are split evenly over the device's resident waves; a wave's range spans
+# sequence ends, several short sequences, or (past 64 steps) more than 64
+# pages, and with fewer steps than waves most ranges are empty
+# --------------------------------------------------------------------------
+
+def lens_case(env, Hq, lens, max_context, P=16, h=128, rot=O.ROT_K, seqs=None, wid=90,
+              masked=3):
+    wl = small(B=len(lens), Hq=Hq, ctx=("list", tuple(int(v) for v in lens)), P=P, h=h,
+               rot_mode=rot, wid=wid, masked=masked)
+    x = widen_tables(W.attn_inputs(wl), max_context)
+    L = x["context_lens"]
+    say(f"attn lens case B={len(L)} Hq={Hq} P={P} tokens={int(np.clip(L, 0, None).sum())} "
+        f"max_context={max_context} rot={ROTS[rot]} h={h}")
+    got = run_gpu(env, x, max_context, h, rot)
+    sel = np.arange(len(L)) if seqs is None else np.asarray(seqs)
+    ref = run_oracle(x, h, rot, seqs=sel, max_context=max_context)
+    check(got[sel], ref, tolerance(x, h, rot, sel, ref, max_context=max_context),
+          f"lens case B={len(L)} Hq={Hq} P={P}")
+    return got
+
+
+@pytest.mark.parametrize("Hq", [8, 32, 64])
+def test_lean_many_short_sequences(env, Hq):
+    # 1024 sequences of 0-300 tokens (about one in seven empty): ranges of
+    # about 13 steps cross several sequences each
+    rng = np.random.default_rng(Hq)
+    lens = np.where(rng.random(1024) < 0.15, 0, rng.integers(1, 301, size=1024))
+    lens[-3:] = 0                                   # empty sequences at the end
+    got = lens_case(env, Hq, lens, 768, wid=91 + Hq)
+    assert not got[lens == 0].any()
+
+
+def test_lean_page_64_kv_rotation(env):
+    rng = np.random.default_rng(3)
+    lens = np.where(rng.random(1024) < 0.1, 0, rng.integers(1, 301, size=1024))
+    lens_case(env, 32, lens, 768, P=64, rot=O.ROT_KV, h=32, wid=94)
+
+
+def test_lean_fewer_steps_than_waves(env):
+    # 64 sequences of 0-40 tokens under max_context 16384: about 90 steps for
+    # hundreds of waves per head pair
+    rng = np.random.default_rng(7)
+    lens = rng.integers(0, 41, size=64)
+    lens[:2] = 0
+    lens_case(env, 32, lens, 16384, rot=O.ROT_KV, h=64, wid=95)
+
+
+@pytest.mark.parametrize("Hq", [32, 64])
+def test_lean_ranges_over_many_pages(env, Hq):
+    # 32 contexts of 24 000-32 768 tokens with 16-token pages: 80-130 steps
+    # per wave, so ranges span more than 64 pages (page ids held 64 at a time)
+    rng = np.random.default_rng(Hq + 1)
+    lens = rng.integers(24000, 32769, size=32)
+    seqs = np.unique(np.r_[np.argmin(lens), np.argmax(lens), rng.choice(32, 2, replace=False)])
+    lens_case(env, Hq, lens, 32768, seqs=seqs, wid=96 + Hq, masked=0)
+
+
+def test_more_sequences_than_the_lean_split_takes(env):
+    # 1025 sequences: the chunk form
+    rng = np.random.default_rng(11)
+    lens = rng.integers(0, 64, size=1025)
+    lens_case(env, 32, lens, 768, wid=99)
+
+
+# --------------------------------------------------------------------------
 # full size: 256 sequences, contexts up to 8000, sampled against the oracle
 # --------------------------------------------------------------------------
 
-# 256 sequences: 1024-token chunks; 128: 512-token chunks
-@pytest.mark.parametrize("B", [256, 128])
+# 256 and 128 sequences: the lean split; 64: the chunk form (512-token chunks)
+@pytest.mark.parametrize("B", [256, 128, 64])
 def test_full_size_sampled(env, B):
     wl = W.ATTN_WORKLOADS["attn"]
     x = W.attn_inputs(wl)
