@@ -292,10 +292,11 @@ int sawkv_append_pattern_control(const void* k, const void* v,
  *                 entries past a sequence's last page are never read
  *   context_lens  int32 [B], device memory; values above max_context are
  *                 cut to max_context, negative values count as 0
- *   max_context   also sizes the split of the contexts into chunks and
- *                 decides whether the pool is streamed past the cache
- *                 (B x max_context x H x 132 bytes above 768 MiB): pass the
- *                 batch's longest context, not a loose capacity bound
+ *   max_context   also sizes the split of the contexts (chunks of up to
+ *                 1024 tokens, or, from B x ceil(max_context / 16) >= 49152
+ *                 with B <= 1024 and H even, equal ranges of 16-token steps
+ *                 over the device's resident waves): pass the batch's
+ *                 longest context, not a loose capacity bound
  *   out           fp16 [B][Hq][D] contiguous
  *   workspace     device memory of at least the size that
  *                 sawkv_decode_attention_workspace_size reports for the same

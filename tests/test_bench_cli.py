@@ -25,7 +25,7 @@ def test_traffic_record_follows_the_source_hash(monkeypatch):
     with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
         rec = json.load(f)
     for name, srcs in (("long", bench.KERNEL_SRC), ("prefill", bench.KERNEL_SRC),
-                       ("attn", bench.ATTN_SRC)):
+                       ("attn", bench.ATTN_SRC), ("attn_long", bench.ATTN_SRC)):
         ent = rec[name]
         monkeypatch.setattr(bench, "kernel_source_hash", lambda s=None, h=ent["kernel_source_hash"]: h)
         assert bench.measured_traffic(name, srcs) == ent["bytes_per_launch"]
@@ -33,7 +33,7 @@ def test_traffic_record_follows_the_source_hash(monkeypatch):
         assert bench.measured_traffic(name, srcs) is None
 
 
-@pytest.mark.parametrize("name", ["long", "prefill", "attn"])
+@pytest.mark.parametrize("name", ["long", "prefill", "attn", "attn_long"])
 def test_traffic_record_is_consistent(name):
     with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
         ent = json.load(f)[name]
@@ -42,9 +42,9 @@ def test_traffic_record_is_consistent(name):
         got = (ent["fetch_size_kib_per_dispatch"] * ent["fetch_scale"]
                + ent["write_size_kib_per_dispatch"] * ent["write_scale"]) * kib
     else:
-        got = ((ent["chunk_fetch_size_kib_per_dispatch"] + ent["combine_fetch_size_kib_per_dispatch"])
+        got = ((ent["split_fetch_size_kib_per_dispatch"] + ent["combine_fetch_size_kib_per_dispatch"])
                * ent["fetch_scale"]
-               + (ent["chunk_write_size_kib_per_dispatch"] + ent["combine_write_size_kib_per_dispatch"])
+               + (ent["split_write_size_kib_per_dispatch"] + ent["combine_write_size_kib_per_dispatch"])
                * ent["write_scale"]) * kib
     assert abs(got - ent["bytes_per_launch"]) <= 1e-4 * ent["bytes_per_launch"]
     # traffic can exceed the algorithmic bytes (partials, partial lines) but never undercut
