@@ -1068,7 +1068,12 @@ __device__ __forceinline__ void pair_piece(const ChunkParams& p, const int b, co
   // faster with ordinary loads up to 64 sequences, because it then stays
   // cached between calls.
   constexpr int kAux = 2;
-  const int lane = threadIdx.x;
+  int lane = threadIdx.x;
+  // in the lean kernel's loop over ranges, the lane's load offsets are
+  // derived anew for every piece instead of being held across the loop (the
+  // opaque copy keeps the compiler from hoisting them): eight queries per KV
+  // head then fit 167 registers, three waves per SIMD, instead of 187
+  if constexpr (WINDOWS) asm volatile("" : "+v"(lane));
   const int g = lane >> 4, n = lane & 15;
   const int h0 = 2 * hp;
 
