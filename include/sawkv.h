@@ -293,7 +293,7 @@ int sawkv_append_pattern_control(const void* k, const void* v,
  *   context_lens  int32 [B], device memory; values above max_context are
  *                 cut to max_context, negative values count as 0
  *   max_context   also sizes the split of the contexts (chunks of up to
- *                 1024 tokens, or, from B x ceil(max_context / 16) >= 49152
+ *                 1024 tokens, or, from B x ceil(max_context / 16) >= 40960
  *                 with B <= 1024 and H even, equal ranges of 16-token steps
  *                 over the device's resident waves): pass the batch's
  *                 longest context, not a loose capacity bound

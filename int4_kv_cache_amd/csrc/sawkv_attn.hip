@@ -1587,11 +1587,12 @@ struct Layout {
 // of KV heads (head pairs). Its grid is the resident waves of the device, at
 // most kLeanMaxWaves.
 // Measured on the decode batch (contexts uniform in [1, 8000], page 16), us
-// per call chunk form / lean form: 256 sequences 232.1 / 220.6 (32 query
-// heads), 251.5 / 238.4 (64), 223.1 / 206.3 (8); 128 sequences 122.9 / 120.6,
-// 139.2 / 131.2, 115.3 / 112.3; 64 sequences (32 000 steps) 69.4 / 72.4,
-// 76.5 / 78.6, 65.7 / 66.1; 64 contexts of 32 768 tokens 409.0 / 398.9.
-constexpr int64_t kLeanMinSteps = 49152;
+// per call chunk form / lean form for 32 / 64 / 8 query heads: 256 sequences
+// 232.1 / 214.0, 251.5 / 237.5, 223.1 / 202.6; 96 sequences (48 000 steps)
+// 101.8 / 91.9, 109.0 / 105.6, 94.9 / 85.8; 80 (40 000) 81.2 / 80.9, 94.4 /
+// 94.2, 75.4 / 75.5; 64 70.2 / 69.7, 77.0 / 82.0, 66.0 / 65.1; 32 43.9 / 46.9,
+// 44.8 / 56.3, 38.6 / 42.8; 64 contexts of 32 768 tokens 409.0 / 382.8.
+constexpr int64_t kLeanMinSteps = 40960;
 constexpr int kLeanMaxWaves = 4096;
 
 bool lean_sizes(int64_t B, int32_t H, int64_t max_context) {

@@ -324,7 +324,7 @@ def test_append_then_attention(env):
 
 
 # --------------------------------------------------------------------------
-# the lean split: from 49 152 steps of 16 tokens (B * ceil(max_context / 16))
+# the lean split: from 40 960 steps of 16 tokens (B * ceil(max_context / 16))
 # up to 1024 sequences with an even KV-head count, the step's 16-token steps
 # are split evenly over the device's resident waves; a wave's range spans
 # sequence ends, several short sequences, or (past 64 steps) more than 64
