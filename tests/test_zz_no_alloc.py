@@ -45,7 +45,7 @@ def _both(env, d, B, max_context, h, rot):
 
 
 @pytest.mark.parametrize("name,first,second", [
-    ("attn", 256, 40),          # 68 MB of partials, then a smaller batch
+    ("attn", 256, 40),          # the lean split, then the chunk form on fewer sequences
     ("attn_small", 9, 4),       # ragged, empty and masked contexts
 ])
 def test_noalloc_equals_workspace_call(env, name, first, second):
@@ -77,13 +77,15 @@ def test_noalloc_rejects_sizes_beyond_the_scratch(env):
     assert e.value.status == S.EUNSUPPORTED
 
 
-def test_noalloc_replays_under_graph_capture(env):
+@pytest.mark.parametrize("name", ["attn_small", "attn"])
+def test_noalloc_replays_under_graph_capture(env, name):
     """The callers it is for: the no-alloc call captured into a HIP graph
     (after one eager call, which looks up the scratch address). Every replay,
     with fresh queries written in place beforehand and eager calls of both
-    entry points in between, equals those eager calls byte for byte."""
+    entry points in between, equals those eager calls byte for byte. The small
+    batch runs the chunk form, the 256-sequence one the lean split."""
     torch, S = env
-    wl = W.ATTN_WORKLOADS["attn_small"]
+    wl = W.ATTN_WORKLOADS[name]
     x = W.attn_inputs(wl)
     d = _dev(torch, x)
     pools = (d["k_codes"], d["v_codes"], d["k_scales"], d["v_scales"])
@@ -102,7 +104,7 @@ def test_noalloc_replays_under_graph_capture(env):
         fresh = rng.standard_normal(tuple(q.shape)).astype(np.float16)
         q.copy_(torch.from_numpy(fresh).cuda())
         torch.cuda.synchronize()
-        say(f"graph replay {i}")
+        say(f"graph replay {i} ({name})")
         g.replay()
         torch.cuda.synchronize()
         got = out.cpu().numpy()
