@@ -302,6 +302,29 @@ def test_attention_workspace_follows_the_chunk_rule(lib, B, H, maxc, C):
     assert n == align(B * nc * Hq * 2 * 4) + align(B * nc * Hq * 128 * 4)
 
 
+@pytest.mark.parametrize("B,Hq,H,maxc,lean", [
+    (1024, 32, 8, 640, True),     # 40 960 steps of 16 tokens: the lean split may run
+    (1024, 32, 8, 624, False),    # 39 936 steps: the chunk form only
+    (1025, 32, 8, 1000, False),   # more than 1024 sequences: the chunk form only
+    (1024, 28, 7, 640, False),    # odd KV-head count: no head pairs, the chunk form only
+])
+def test_attention_workspace_covers_the_lean_split(lib, B, Hq, H, maxc, lean):
+    """Where the lean split may run, the workspace also holds its layout: 8 bytes
+    per sequence for the merge's view, then the partials of (sequence, wave)
+    rows b + k, at most B + 4096 / (H / 2) of them per query head."""
+    st, n = attn_ws(lib, B=B, Hq=Hq, H=H, maxc=maxc)
+    assert st == OK
+    align = lambda x: (x + 255) // 256 * 256
+    rows = (B + 4096 // (H // 2)) * Hq
+    lean_bytes = align(B * 8) + align(rows * 2 * 4) + align(rows * 128 * 4)
+    if lean:
+        assert n >= lean_bytes
+    else:
+        # the chunk form's layout alone: (max, sum) pairs and outputs of whole chunks
+        per = n // (Hq * (2 + 128) * 4)
+        assert n == align(per * Hq * 2 * 4) + align(per * Hq * 128 * 4)
+
+
 # ---- controls: uncompressed cache write and token-wise INT8 (validation only) ----
 
 def ctl(lib, name, **kw):
