@@ -294,9 +294,10 @@ int sawkv_append_pattern_control(const void* k, const void* v,
  *                 cut to max_context, negative values count as 0
  *   max_context   also sizes the split of the contexts (chunks of up to
  *                 1024 tokens, or, from B x ceil(max_context / 16) >= 40960
- *                 with B <= 1024 and H even, equal ranges of 16-token steps
- *                 over the device's resident waves): pass the batch's
- *                 longest context, not a loose capacity bound
+ *                 with B <= 1024, equal ranges of 16-token steps over the
+ *                 device's resident waves; for an odd H also at least 128
+ *                 such steps per wave): pass the batch's longest context,
+ *                 not a loose capacity bound
  *   out           fp16 [B][Hq][D] contiguous
  *   workspace     device memory of at least the size that
  *                 sawkv_decode_attention_workspace_size reports for the same

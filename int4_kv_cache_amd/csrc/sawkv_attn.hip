@@ -507,9 +507,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 
 // Issues the loads of the step at t0 into r. `pages` holds the page id of
 // block (blk0 + lane) of the sequence in lane `lane`.
-template <bool BRANCHLESS>
+// WIN: the page ids of the range are held 64 at a time, those of pages
+// blk0 .. blk0 + 63 in `pages`, the next 64 in `pages_next`; a step's two
+// tiles may fall on either side of that boundary.
+template <bool BRANCHLESS, bool WIN = false>
 __device__ __forceinline__ void load_step(const ChunkParams& p, StepRegs& r, int t0, int t_end,
-                                          int blk0, int pages, int h, const Lanes& ln) {
+                                          int blk0, int pages, int h, const Lanes& ln,
+                                          int pages_next = -1) {
   const uint32_t row_bytes = (uint32_t)p.H * (kD / 2);
   const uint32_t tile_bytes = 15u * row_bytes + kD / 2;      // reach of a lane's offsets
   int64_t row[2];                                 // first row of each tile (0 if invalid)
@@ -517,7 +521,14 @@ __device__ __forceinline__ void load_step(const ChunkParams& p, StepRegs& r, int
   for (int T = 0; T < 2; ++T) {
     const int st = t0 + 16 * T;
     int page = -1;
-    if (st < t_end) page = __builtin_amdgcn_readlane(pages, st / p.P - blk0);
+    if (st < t_end) {
+      const int idx = st / p.P - blk0;
+      if constexpr (WIN)
+        page = idx < 64 ? __builtin_amdgcn_readlane(pages, idx & 63)
+                        : __builtin_amdgcn_readlane(pages_next, (idx - 64) & 63);
+      else
+        page = __builtin_amdgcn_readlane(pages, idx);
+    }
     r.ok[T] = page >= 0 && page < p.N_pg;
     const int64_t row0 = r.ok[T] ? ((int64_t)page * p.P + st % p.P) * p.H + h : 0;
     row[T] = row0;
@@ -683,47 +694,32 @@ __device__ __forceinline__ void compute_step(const StepRegs& r, const uint32_t (
   }
 }
 
-template <int G, bool EARLY>
-__global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
+// Tokens [t_begin, t_end) of sequence b for KV head h, one wave: the
+// partial (reference exponent, denominator, weighted values) of the head's G
+// queries goes to partial row `part`. t_begin is a multiple of 16. WINDOWS:
+// the range may span more than 64 pages (page ids held 64 at a time).
+template <int G, bool EARLY, bool WINDOWS>
+__device__ __forceinline__ void head_piece(const ChunkParams& p, const int b, const int h,
+                                           const int t_begin, const int t_end,
+                                           const int64_t part, uint16_t* sstage,
+                                           float (*xs)[kD]) {
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
-  __shared__ uint16_t sstage[64];
-  __shared__ float xs[G][kD];
-  const int lane = threadIdx.x;
+  int lane = threadIdx.x;
+  // in the lean kernel's loop over ranges, the lane's offsets are derived
+  // anew for every piece rather than held across the loop
+  if constexpr (WINDOWS) asm volatile("" : "+v"(lane));
   const int g = lane >> 4, n = lane & 15;
 
-  // Block -> (chunk, sequence, head). Blocks are dealt to the 8 XCDs in turn
-  // (block i to XCD i % 8); the H heads of one (sequence, chunk) get
-  // consecutive blocks of one XCD, so the 64-byte rows of neighbouring heads,
-  // which share cache lines, meet in one L2.
-  const uint32_t bx = blockIdx.x;
-  const uint32_t r8 = bx >> 3;
-  const int h = (int)(r8 % (uint32_t)p.H);
-  const uint32_t grp = (r8 / (uint32_t)p.H) * 8u + (bx & 7u);
-  if (grp >= p.n_groups) return;
-  // Groups of chunks in dispatch order, counted from the end of each context:
-  // group r holds chunk nck - NC + r of every sequence (nck = its chunk
-  // count), so whole chunks go first and the partial last chunks (r = NC - 1)
-  // last, which keeps the final round of waves short (longest work first).
-  const uint32_t nb = p.n_groups / (uint32_t)p.NC;
-  // the groups of XCD x are those with grp % 8 == x; offsetting the sequence
-  // by r spreads the chunks of one sequence over the XCDs (when nb % 8 == 0
-  // group r of sequence b goes to XCD (b + r) % 8), so every XCD gets a share
-  // of every context, not whole ones
-  const int r = (int)(grp / nb);
-  const int b = (int)((grp % nb + nb - (uint32_t)r % nb) % nb);
-  int L = p.context_lens[b];
-  L = L < 0 ? 0 : (L > p.max_context ? p.max_context : L);
-  const int c = (L + p.C - 1) / p.C - p.NC + r;     // chunk index; < 0: none
-  if (c < 0) return;
-  const uint32_t part = (uint32_t)b * p.NC + c;    // partial slot (b, c)
-  const int t_begin = c * p.C;
-  if (t_begin >= L) return;
-  const int t_end = min(t_begin + p.C, L);
-
-  // page ids of the chunk's blocks, one per lane (at most 64, see make_layout)
-  const int blk0 = t_begin / p.P;
-  const int n_blk = (t_end - 1) / p.P - blk0 + 1;
-  const int pages = lane < n_blk ? p.block_tables[(int64_t)b * p.bt_stride + blk0 + lane] : -1;
+  // page ids of the range's blocks, one per lane, 64 at a time (a chunk
+  // spans at most 64, see make_layout)
+  int blk0 = t_begin / p.P;
+  const int blk_last = (t_end - 1) / p.P;
+  const int32_t* bt_row = p.block_tables + (int64_t)b * p.bt_stride;
+  int pages = lane <= blk_last - blk0 ? bt_row[blk0 + lane] : -1;
+  int pages_next = -1;
+  if constexpr (WINDOWS) {
+    if (blk_last - blk0 >= 64) pages_next = lane <= blk_last - blk0 - 64 ? bt_row[blk0 + 64 + lane] : -1;
+  }
   // the query's load goes out between the page ids and the first step, so
   // each wait takes only what it needs (loads complete in issue order)
   const QueryRaw<G, false> qraw = load_query<G, false>(p.qp, b, h, lane);
@@ -751,16 +747,28 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
   u4_t bq[4];
   float cinit, F;
   if constexpr (EARLY) {
-    load_step<true>(p, cur, t_begin, t_end, blk0, pages, h, ln);
+    load_step<true, WINDOWS>(p, cur, t_begin, t_end, blk0, pages, h, ln, pages_next);
     prepare_query<G, false>(p.qp, qraw, lane, xs, bq, cinit, F);
   } else {
     prepare_query<G, false>(p.qp, qraw, lane, xs, bq, cinit, F);
-    load_step<false>(p, cur, t_begin, t_end, blk0, pages, h, ln);
+    load_step<false, WINDOWS>(p, cur, t_begin, t_end, blk0, pages, h, ln, pages_next);
   }
   const float F4 = 4.0f * F;
   for (int t0 = t_begin; t0 < t_end; t0 += kStep) {
     const int t1 = t0 + kStep;
-    if (t1 < t_end) load_step<false>(p, nxt, t1, t_end, blk0, pages, h, ln);
+    if (t1 < t_end) {
+      if constexpr (WINDOWS) {
+        // the next step's first tile opens the next 64 pages (wave-uniform):
+        // their ids were loaded with the previous window's, the following
+        // ones go out now, 64 pages before a tile needs them
+        if (t1 / p.P - blk0 >= 64) {
+          blk0 += 64;
+          pages = pages_next;
+          pages_next = lane <= blk_last - blk0 - 64 ? bt_row[blk0 + 64 + lane] : -1;
+        }
+      }
+      load_step<false, WINDOWS>(p, nxt, t1, t_end, blk0, pages, h, ln, pages_next);
+    }
     sstage[lane] = (uint16_t)cur.sc;
     __builtin_amdgcn_wave_barrier();
     uint32_t ks[2][2], vs[2][2];
@@ -801,7 +809,7 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
   }
   const int Wb = __builtin_bit_cast(int, W);
 
-  const int64_t head0 = (int64_t)part * p.Hq + (int64_t)h * G;
+  const int64_t head0 = part * p.Hq + (int64_t)h * G;
   const bool writer = G == 8 ? g < 2 : g == 0;
   if (writer) {
 #pragma unroll
@@ -828,6 +836,45 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
     p.part_ml[(head0 + n) * 2] = a.m == -INFINITY ? -INFINITY : a.mref;
     p.part_ml[(head0 + n) * 2 + 1] = l;
   }
+}
+
+// One (chunk, sequence, KV head) per block: chunk c covers tokens
+// [c C, (c + 1) C) of the sequence.
+template <int G, bool EARLY>
+__global__ __launch_bounds__(64) void attn_chunk_kernel(ChunkParams p) {
+  __shared__ uint16_t sstage[64];
+  __shared__ float xs[G][kD];
+
+  // Block -> (chunk, sequence, head). Blocks are dealt to the 8 XCDs in turn
+  // (block i to XCD i % 8); the H heads of one (sequence, chunk) get
+  // consecutive blocks of one XCD, so the 64-byte rows of neighbouring heads,
+  // which share cache lines, meet in one L2.
+  const uint32_t bx = blockIdx.x;
+  const uint32_t r8 = bx >> 3;
+  const int h = (int)(r8 % (uint32_t)p.H);
+  const uint32_t grp = (r8 / (uint32_t)p.H) * 8u + (bx & 7u);
+  if (grp >= p.n_groups) return;
+  // Groups of chunks in dispatch order, counted from the end of each context:
+  // group r holds chunk nck - NC + r of every sequence (nck = its chunk
+  // count), so whole chunks go first and the partial last chunks (r = NC - 1)
+  // last, which keeps the final round of waves short (longest work first).
+  const uint32_t nb = p.n_groups / (uint32_t)p.NC;
+  // the groups of XCD x are those with grp % 8 == x; offsetting the sequence
+  // by r spreads the chunks of one sequence over the XCDs (when nb % 8 == 0
+  // group r of sequence b goes to XCD (b + r) % 8), so every XCD gets a share
+  // of every context, not whole ones
+  const int r = (int)(grp / nb);
+  const int b = (int)((grp % nb + nb - (uint32_t)r % nb) % nb);
+  int L = p.context_lens[b];
+  L = L < 0 ? 0 : (L > p.max_context ? p.max_context : L);
+  const int c = (L + p.C - 1) / p.C - p.NC + r;     // chunk index; < 0: none
+  if (c < 0) return;
+  const int64_t part = (int64_t)b * p.NC + c;      // partial slot (b, c)
+  const int t_begin = c * p.C;
+  if (t_begin >= L) return;
+  const int t_end = min(t_begin + p.C, L);
+
+  head_piece<G, EARLY, false>(p, b, h, t_begin, t_end, part, sstage, xs);
 }
 
 // ---------------------------------------------------------------------------
@@ -1284,20 +1331,15 @@ __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
 // floor(((s + 1) n - 1) / S). Wave 0 marks the empty sequences.
 constexpr int kLeanMaxB = 1024;
 
-template <int GR>
-__global__ __launch_bounds__(64) void attn_lean_pair_kernel(ChunkParams p) {
-  __shared__ uint16_t sstage[64];
-  __shared__ float xs[2 * pair_slots<GR>()][kD];
-  const int HP = p.H / 2;
+// The split for wave k of n (n = p.lean_waves): returns false if the step has
+// no token; else b, s0 = the sequence and local step where the range starts
+// and rem = its length in steps (0: an empty range). `writer`: this wave
+// records the merge's view of the sequences whose first step lies in its
+// range (one head group's waves do).
+__device__ __forceinline__ bool lean_range(const ChunkParams& p, const int k, const bool writer,
+                                           int& b, int& s0, int64_t& rem) {
   const int lane = threadIdx.x;
-  // block -> (wave k, head pair): the pairs of one range on one XCD
-  const uint32_t bx = blockIdx.x;
-  const uint32_t r8 = bx >> 3;
-  const int hp = (int)(r8 % (uint32_t)HP);
-  const int k = (int)((r8 / (uint32_t)HP) * 8u + (bx & 7u));
   const int N = p.lean_waves;
-  if (k >= N) return;
-
   // steps of the lane's sequences 16 lane + j, and their sum
   int st[16];
   int lsum = 0;
@@ -1319,8 +1361,7 @@ __global__ __launch_bounds__(64) void attn_lean_pair_kernel(ChunkParams p) {
   const int64_t S = __builtin_amdgcn_readlane(incl, 63);
   const int64_t lo = S > 0 ? (int64_t)k * S / N : 0;
   const int64_t hi = S > 0 ? (int64_t)(k + 1) * S / N : 0;
-  if (hp == 0) {
-    // the merge's view of the lane's sequences
+  if (writer) {
     int pre = 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -1337,12 +1378,14 @@ __global__ __launch_bounds__(64) void attn_lean_pair_kernel(ChunkParams p) {
       pre += st[j];
     }
   }
-  if (S == 0) return;
+  if (S == 0) return false;
   // the sequence holding step lo: its lane, then its place in the lane
   const uint64_t ball = __ballot(excl <= lo && lo < (int64_t)excl + lsum);
   const int lam = __ffsll((unsigned long long)ball) - 1;
   const int off = (int)(lo - __builtin_amdgcn_readlane(excl, lam));
-  int b = -1, s0 = 0, pre = 0;
+  b = -1;
+  s0 = 0;
+  int pre = 0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int sj = __builtin_amdgcn_readlane(st[j], lam);
@@ -1352,24 +1395,21 @@ __global__ __launch_bounds__(64) void attn_lean_pair_kernel(ChunkParams p) {
     }
     pre += sj;
   }
-  int64_t rem = hi - lo;
-  if (rem == 0) {
-    // an empty partial (no token) for every query of the pair
-    if (lane < 2 * GR) {
-      const int64_t row = ((int64_t)b + k) * p.Hq + (int64_t)2 * hp * GR + lane;
-      p.part_ml[row * 2] = -INFINITY;
-      p.part_ml[row * 2 + 1] = 0.0f;
-    }
-    return;
-  }
+  rem = hi - lo;
+  return true;
+}
+
+// Walks wave k's range from (b, s0) for rem steps, one piece per sequence:
+// piece(b, t_begin, t_end) for each.
+template <typename Piece>
+__device__ __forceinline__ void lean_walk(const ChunkParams& p, int b, int s0, int64_t rem,
+                                          Piece&& piece) {
   for (;;) {
     int L = p.context_lens[b];
     L = L < 0 ? 0 : (L > p.max_context ? p.max_context : L);
     const int steps = (L + 15) >> 4;
     const int nstep = (int)min((int64_t)(steps - s0), rem);
-    const int t_begin = 16 * s0;
-    const int t_end = min(16 * (s0 + nstep), L);
-    pair_piece<GR, true, true>(p, b, hp, t_begin, t_end, (int64_t)b + k, sstage, xs);
+    piece(b, 16 * s0, min(16 * (s0 + nstep), L));
     rem -= nstep;
     if (rem <= 0) break;
     // the next sequence with a token (the range ends inside one)
@@ -1380,6 +1420,61 @@ __global__ __launch_bounds__(64) void attn_lean_pair_kernel(ChunkParams p) {
     }
     s0 = 0;
   }
+}
+
+// An empty partial (no token) for `nq` queries from query head q0 in row `row`.
+__device__ __forceinline__ void lean_empty(const ChunkParams& p, int64_t row, int q0, int nq) {
+  if ((int)threadIdx.x < nq) {
+    const int64_t r = row * p.Hq + q0 + threadIdx.x;
+    p.part_ml[r * 2] = -INFINITY;
+    p.part_ml[r * 2 + 1] = 0.0f;
+  }
+}
+
+template <int GR>
+__global__ __launch_bounds__(64) void attn_lean_pair_kernel(ChunkParams p) {
+  __shared__ uint16_t sstage[64];
+  __shared__ float xs[2 * pair_slots<GR>()][kD];
+  const int HP = p.H / 2;
+  // block -> (wave k, head pair): the pairs of one range on one XCD
+  const uint32_t bx = blockIdx.x;
+  const uint32_t r8 = bx >> 3;
+  const int hp = (int)(r8 % (uint32_t)HP);
+  const int k = (int)((r8 / (uint32_t)HP) * 8u + (bx & 7u));
+  if (k >= p.lean_waves) return;
+  int b, s0;
+  int64_t rem;
+  if (!lean_range(p, k, hp == 0, b, s0, rem)) return;
+  if (rem == 0) {
+    lean_empty(p, (int64_t)b + k, 2 * hp * GR, 2 * GR);
+    return;
+  }
+  lean_walk(p, b, s0, rem, [&](int bb, int t_begin, int t_end) {
+    pair_piece<GR, true, true>(p, bb, hp, t_begin, t_end, (int64_t)bb + k, sstage, xs);
+  });
+}
+
+// The same split for an odd number of KV heads: one wave per (range, head).
+template <int G>
+__global__ __launch_bounds__(64) void attn_lean_kernel(ChunkParams p) {
+  __shared__ uint16_t sstage[64];
+  __shared__ float xs[G][kD];
+  // block -> (wave k, head): the heads of one range on one XCD
+  const uint32_t bx = blockIdx.x;
+  const uint32_t r8 = bx >> 3;
+  const int h = (int)(r8 % (uint32_t)p.H);
+  const int k = (int)((r8 / (uint32_t)p.H) * 8u + (bx & 7u));
+  if (k >= p.lean_waves) return;
+  int b, s0;
+  int64_t rem;
+  if (!lean_range(p, k, h == 0, b, s0, rem)) return;
+  if (rem == 0) {
+    lean_empty(p, (int64_t)b + k, h * G, G);
+    return;
+  }
+  lean_walk(p, b, s0, rem, [&](int bb, int t_begin, int t_end) {
+    head_piece<G, true, true>(p, bb, h, t_begin, t_end, (int64_t)bb + k, sstage, xs);
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -1583,9 +1678,10 @@ struct Layout {
 // The lean form (equal steps per wave, see attn_lean_pair_kernel) serves
 // steps with many tokens per head pair: at least kLeanMinSteps 16-token steps
 // if every sequence had max_context tokens (fewer than 2^31, counted in 32
-// bits), at most kLeanMaxB sequences (16 per lane of a wave), an even number
-// of KV heads (head pairs). Its grid is the resident waves of the device, at
-// most kLeanMaxWaves.
+// bits), at most kLeanMaxB sequences (16 per lane of a wave); one wave per
+// (range, head pair) for an even number of KV heads, per (range, head) for an
+// odd one. Its grid is the resident waves of the device, at most
+// kLeanMaxWaves.
 // Measured on the decode batch (contexts uniform in [1, 8000], page 16), us
 // per call chunk form / lean form for 32 / 64 / 8 query heads: 256 sequences
 // 232.1 / 214.0, 251.5 / 237.5, 223.1 / 202.6; 96 sequences (48 000 steps)
@@ -1593,13 +1689,24 @@ struct Layout {
 // 94.2, 75.4 / 75.5; 64 70.2 / 69.7, 77.0 / 82.0, 66.0 / 65.1; 32 43.9 / 46.9,
 // 44.8 / 56.3, 38.6 / 42.8; 64 contexts of 32 768 tokens 409.0 / 382.8.
 constexpr int64_t kLeanMinSteps = 40960;
+// One wave per (range, head) for odd head counts takes the lean split only
+// with at least kLeanMinHeadSteps steps per wave if every sequence had
+// max_context tokens (its loop steps are 32 tokens; fewer per wave lose to
+// the chunk form). Measured, contexts uniform in [1, 8000], us per call cold,
+// chunk form / lean split: 1 KV head (3072 waves) 256 sequences (42 steps per
+// wave) 47.8 / 51.9, 1024 sequences (167) 141.1 / 129.1; 3 KV heads (1024
+// waves per head) 256 sequences (125) 113.1 / 114.6, 1024 (500) 395.2 / 377.4.
+constexpr int64_t kLeanMinHeadSteps = 128;
 constexpr int kLeanMaxWaves = 4096;
 
-bool lean_sizes(int64_t B, int32_t H, int64_t max_context) {
+bool lean_sizes(int64_t B, int64_t max_context) {
   const int64_t steps = B * ((max_context + 15) / 16);
-  return H % 2 == 0 && B > 0 && B <= sawkv::attn::kLeanMaxB && steps >= kLeanMinSteps &&
+  return B > 0 && B <= sawkv::attn::kLeanMaxB && steps >= kLeanMinSteps &&
          steps < (INT64_C(1) << 31);
 }
+
+// head groups of one wave: pairs of KV heads when H is even, else single heads
+int32_t head_groups(int32_t H) { return H % 2 == 0 ? H / 2 : H; }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -1635,9 +1742,9 @@ Layout make_layout(int64_t B, int32_t Hq, int32_t H, int64_t max_context) {
   L.o = off;
   off = align256(off + (size_t)B * L.NC * Hq * sawkv::kD * 4);
   L.total = off;
-  L.lean = lean_sizes(B, H, max_context);
+  L.lean = lean_sizes(B, max_context);
   if (L.lean) {
-    L.lean_waves = kLeanMaxWaves / (H / 2);
+    L.lean_waves = std::max(8, kLeanMaxWaves / head_groups(H));
     const size_t rows = (size_t)(B + L.lean_waves) * Hq;   // partial rows b + k
     size_t lo = 0;
     L.l_seq = lo;
@@ -1711,20 +1818,25 @@ constexpr int64_t kEarlyIssueBlocks = 4 * 3 * 4 * 256;
 // 137, 96 (6144) 114 / 110, 64 (4096) 76 / 78, 16 34 / 37, 1 12.5 / 15.4.
 constexpr int64_t kPairEightBlocks = 2 * 3 * 4 * 256;
 
+using sawkv::attn::attn_lean_kernel;
 using sawkv::attn::attn_lean_pair_kernel;
 
-const void* const kLeanPair[4] = {(void*)&attn_lean_pair_kernel<1>, (void*)&attn_lean_pair_kernel<2>,
-                                  (void*)&attn_lean_pair_kernel<4>, (void*)&attn_lean_pair_kernel<8>};
+// [head pairs][G index]
+const void* const kLean[2][4] = {
+    {(void*)&attn_lean_kernel<1>, (void*)&attn_lean_kernel<2>, (void*)&attn_lean_kernel<4>,
+     (void*)&attn_lean_kernel<8>},
+    {(void*)&attn_lean_pair_kernel<1>, (void*)&attn_lean_pair_kernel<2>,
+     (void*)&attn_lean_pair_kernel<4>, (void*)&attn_lean_pair_kernel<8>}};
 
-// Lean waves per head pair on the device of `stream`: the waves the device
+// Lean waves per head group on the device of `stream`: the waves the device
 // keeps resident at once (occupancy of the lean kernel times compute units,
-// asked once per device and grouping), at most kLeanMaxWaves over all pairs
-// and max_per_pair per pair, a multiple of 8; 0 if the device cannot say.
+// asked once per device and kernel), at most kLeanMaxWaves over all groups
+// and max_per_group per group, a multiple of 8; 0 if the device cannot say.
 constexpr int kLeanDevices = 64;
 std::mutex g_lean_mu;
-int g_lean_resident[kLeanDevices][4] = {};
+int g_lean_resident[kLeanDevices][2][4] = {};
 
-int lean_waves_per_pair(hipStream_t stream, int gi, int HP, int max_per_pair) {
+int lean_waves_per_group(hipStream_t stream, int pair, int gi, int groups, int max_per_group) {
   int dev = -1;
   if ((stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev)) != hipSuccess || dev < 0 ||
       dev >= kLeanDevices)
@@ -1732,19 +1844,19 @@ int lean_waves_per_pair(hipStream_t stream, int gi, int HP, int max_per_pair) {
   int resident;
   {
     std::lock_guard<std::mutex> lock(g_lean_mu);
-    resident = g_lean_resident[dev][gi];
+    resident = g_lean_resident[dev][pair][gi];
     if (resident == 0) {
       int per_cu = 0, cus = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kLeanPair[gi], 64, 0) != hipSuccess ||
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kLean[pair][gi], 64, 0) != hipSuccess ||
           hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         per_cu = cus = 0;
       resident = per_cu > 0 && cus > 0 ? per_cu * cus : -1;
-      g_lean_resident[dev][gi] = resident;
+      g_lean_resident[dev][pair][gi] = resident;
     }
   }
   if (resident <= 0) return 0;
-  const int per_pair = std::min(std::min(resident, kLeanMaxWaves) / HP, max_per_pair);
-  return per_pair / 8 * 8;
+  const int per_group = std::min(std::min(resident, kLeanMaxWaves) / groups, max_per_group);
+  return per_group / 8 * 8;
 }
 
 const void* const kCombine[2][5] = {
@@ -1850,14 +1962,18 @@ int attention_impl(const void* q, int64_t q_stride, const void* k_codes, const v
   mp.max_context = (int32_t)max_context;
 
   // the lean form: split plan, equal-steps waves, merge
-  const int nwp = lay.lean ? lean_waves_per_pair(s, g_index(G), H / 2, lay.lean_waves) : 0;
-  if (nwp >= 8) {
+  const int lean_pair = H % 2 == 0 ? 1 : 0;
+  const int nwp = lay.lean ? lean_waves_per_group(s, lean_pair, g_index(G), head_groups(H),
+                                                   lay.lean_waves)
+                           : 0;
+  if (nwp >= 8 && (lean_pair || B * ((max_context + 15) / 16) >= kLeanMinHeadSteps * nwp)) {
     cp.part_o = reinterpret_cast<float*>(ws + lay.l_o);
     cp.part_ml = reinterpret_cast<float*>(ws + lay.l_ml);
     cp.lean_waves = nwp;
     cp.lean_seqs = (int32_t)B;
     cp.lean_seq = reinterpret_cast<int2*>(ws + lay.l_seq);
-    if ((st = launch64(kLeanPair[g_index(G)], (int64_t)nwp * (H / 2), &cp, s))) return st;
+    if ((st = launch64(kLean[lean_pair][g_index(G)], (int64_t)nwp * head_groups(H), &cp, s)))
+      return st;
     mp.part_o = cp.part_o;
     mp.part_ml = cp.part_ml;
     mp.lean_seq = cp.lean_seq;

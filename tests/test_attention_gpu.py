@@ -383,6 +383,41 @@ def test_lean_ranges_over_many_pages(env, Hq):
     lens_case(env, Hq, lens, 32768, seqs=seqs, wid=96 + Hq, masked=0)
 
 
+# odd KV-head counts (a tensor-parallel shard's one or three heads): one wave per
+# (range, head), from 128 steps per wave if every context had max_context
+# tokens; 1024 sequences of 0-300 tokens under max_context 8192 leave most of
+# the 3072 (one head) or 1024 (three heads) waves per head with one step or none
+@pytest.mark.parametrize("Hq,H", [(4, 1), (8, 1), (12, 3)])
+def test_lean_single_head(env, Hq, H):
+    rng = np.random.default_rng(Hq + H)
+    lens = np.where(rng.random(1024) < 0.15, 0, rng.integers(1, 301, size=1024))
+    wl = small(B=1024, Hq=Hq, H=H, ctx=("list", tuple(int(v) for v in lens)),
+               rot_mode=O.ROT_KV, wid=100 + Hq)
+    x = widen_tables(W.attn_inputs(wl), 8192)
+    say(f"attn lean single-head B=1024 Hq={Hq} H={H}")
+    got = run_gpu(env, x, 8192, 128, O.ROT_KV)
+    ref = run_oracle(x, 128, O.ROT_KV, max_context=8192)
+    check(got, ref, tolerance(x, 128, O.ROT_KV, np.arange(1024), ref, max_context=8192),
+          f"lean single-head Hq={Hq} H={H}")
+
+
+def test_lean_single_head_ranges_over_many_pages(env):
+    # 64 contexts of 30 000-32 768 tokens over 3 KV heads with 16-token pages
+    # (131 072 steps at most, 128 per wave for 1024 waves per head): about 120
+    # steps per wave, so a range's 32-token steps cross the 64-page
+    # boundary of its page ids (a step's two tiles on either side of it)
+    rng = np.random.default_rng(31)
+    lens = rng.integers(30000, 32769, size=64)
+    wl = small(B=64, Hq=12, H=3, ctx=("list", tuple(int(v) for v in lens)), rot_mode=O.ROT_K,
+               wid=113, masked=0)
+    x = widen_tables(W.attn_inputs(wl), 32768)
+    say("attn lean single-head B=64 Hq=12 H=3 long contexts")
+    got = run_gpu(env, x, 32768, 128, O.ROT_K)
+    seqs = np.unique(np.r_[np.argmin(lens), np.argmax(lens), rng.choice(64, 2, replace=False)])
+    ref = run_oracle(x, 128, O.ROT_K, seqs=seqs)
+    check(got[seqs], ref, tolerance(x, 128, O.ROT_K, seqs, ref), "lean single-head long")
+
+
 def test_more_sequences_than_the_lean_split_takes(env):
     # 1025 sequences: the chunk form
     rng = np.random.default_rng(11)
