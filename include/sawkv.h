@@ -45,8 +45,9 @@
  *   - T == 0 returns SAWKV_OK after the size checks, launches nothing and
  *     reads no pointer (NULL tensors are accepted then).
  *   - Caller preconditions not checked: no two tokens of one call share a
- *     slot (which write wins is then unspecified); inputs, outputs and pools
- *     do not overlap; K/V values are finite.
+ *     slot (the shared rows then hold the bytes of either token, or a mix of
+ *     the two at 4-byte granularity; no other row is touched); inputs,
+ *     outputs and pools do not overlap; K/V values are finite.
  *   - Supported sizes: D = 128; h in {16, 32, 64, 128}; 1 <= H <= 256;
  *     T*H < 2^31; token strides < 2^26 elements (SAWKV_EUNSUPPORTED otherwise).
  *   - Alignment: every tensor pointer 16-byte aligned, slot_mapping 8-byte
