@@ -418,6 +418,43 @@ def test_lean_single_head_ranges_over_many_pages(env):
     check(got[seqs], ref, tolerance(x, 128, O.ROT_K, seqs, ref), "lean single-head long")
 
 
+# Seeded random configurations over the dispatch space: head counts even and
+# odd, 1 to 8 queries per KV head, page sizes, block sizes, rotations, batch
+# sizes and max_context bounds from tight to loose (which choose between the
+# chunk form's chunk lengths, the head-pair and single-head kernels, and the
+# lean split). Contexts are short and partly empty, with some masked pages, so
+# the oracle checks every output element.
+def random_case(seed):
+    rng = np.random.default_rng([2026, seed])
+    H = int(rng.choice([1, 2, 3, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    P = int(rng.choice([16, 32, 48, 64]))
+    h = int(rng.choice([16, 32, 64, 128]))
+    rot = int(rng.choice([O.ROT_NONE, O.ROT_K, O.ROT_KV]))
+    B = int(rng.choice([1, 7, 40, 96, 256]))
+    lens = rng.integers(1, 400, size=B)
+    lens[rng.random(B) < 0.1] = 0
+    lens[rng.random(B) < 0.05] = rng.integers(400, 3000)
+    maxc = int(rng.choice([max(int(lens.max()), 1), 16384, 32768]))
+    return H, G, P, h, rot, lens, maxc
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_configurations(env, seed):
+    H, G, P, h, rot, lens, maxc = random_case(seed)
+    wl = small(B=len(lens), Hq=G * H, H=H, P=P, h=h, rot_mode=rot,
+               ctx=("list", tuple(int(v) for v in lens)), wid=200 + seed,
+               masked=min(3, int((lens > 0).sum())))
+    x = widen_tables(W.attn_inputs(wl), maxc)
+    say(f"attn random case {seed}: B={len(lens)} H={H} G={G} P={P} h={h} rot={ROTS[rot]} "
+        f"max_context={maxc} tokens={int(lens.sum())}")
+    got = run_gpu(env, x, maxc, h, rot)
+    ref = run_oracle(x, h, rot, max_context=maxc)
+    check(got, ref, tolerance(x, h, rot, np.arange(len(lens)), ref, max_context=maxc),
+          f"random case {seed}")
+    assert not got[lens == 0].any()
+
+
 def test_more_sequences_than_the_lean_split_takes(env):
     # 1025 sequences: the chunk form
     rng = np.random.default_rng(11)
