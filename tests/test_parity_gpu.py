@@ -157,6 +157,34 @@ def test_ragged_shapes(env, H, T):
     run_case(env, k, v, slots, n_pg, P, 64, O.ROT_K, what=f"ragged-k H={H} T={T}")
 
 
+# Seeded random configurations: head counts from 1 to 32, token counts with
+# ragged tails, page sizes, block sizes and rotations, K or V alone, value
+# magnitudes from 1e-5 to 1e3 with zero vectors, shuffled slots with skipped
+# and out-of-range entries; every pool byte and every read-back row compared.
+@pytest.mark.parametrize("seed", range(16))
+def test_random_configurations(env, seed):
+    rng = np.random.default_rng([2026, 7, seed])
+    H = int(rng.choice([1, 2, 3, 5, 8, 13, 32]))
+    T = int(rng.integers(1, 3001))
+    P = int(rng.choice([1, 8, 16, 32]))
+    h = int(rng.choice([16, 32, 64, 128]))
+    rot = int(rng.choice([O.ROT_NONE, O.ROT_K, O.ROT_KV]))
+    mag = float(rng.choice([1e-5, 1.0, 30.0, 1e3]))
+    # finite inputs (a caller precondition): heavy tails clipped below the fp16 range
+    k = np.clip(rng.standard_normal((T, H, 128)) * mag, -6e4, 6e4).astype(np.float16)
+    v = np.clip(rng.standard_t(4, (T, H, 128)) * mag, -6e4, 6e4).astype(np.float16)
+    zero = rng.random(T) < 0.02
+    k[zero] = 0
+    v[zero] = 0
+    n_pg = (T + P - 1) // P + int(rng.integers(0, 4))
+    slots = rng.permutation(n_pg * P)[:T].astype(np.int64)
+    slots[rng.random(T) < 0.03] = -1
+    slots[rng.random(T) < 0.01] = n_pg * P + 5
+    which = int(rng.integers(0, 3))          # 0 both, 1 K alone, 2 V alone
+    run_case(env, k if which != 2 else None, v if which != 1 else None, slots, n_pg, P, h,
+             rot, what=f"random {seed} H={H} which={which} mag={mag}")
+
+
 def test_strided_views_of_fused_qkv(env):
     torch, S = env
     rng = np.random.default_rng(21)
