@@ -89,6 +89,25 @@ def test_int8_all_block_sizes(env, h, rot):
                 oracle_int8(k, v, slots, n_pg, P, h, rot), f"int8 h={h} rot={rot}")
 
 
+# seeded random shapes, block sizes, rotations and magnitudes
+@pytest.mark.parametrize("seed", range(8))
+def test_int8_random_configurations(env, seed):
+    rng = np.random.default_rng([2026, 8, seed])
+    H = int(rng.choice([1, 2, 3, 8, 13]))
+    T = int(rng.integers(1, 2001))
+    P = int(rng.choice([1, 8, 16]))
+    h = int(rng.choice([16, 32, 64, 128]))
+    rot = int(rng.choice([O.ROT_NONE, O.ROT_K, O.ROT_KV]))
+    mag = float(rng.choice([1e-4, 1.0, 300.0]))
+    k = np.clip(rng.standard_normal((T, H, 128)) * mag, -6e4, 6e4).astype(np.float16)
+    v = np.clip(rng.standard_t(4, (T, H, 128)) * mag, -6e4, 6e4).astype(np.float16)
+    n_pg = (T + P - 1) // P + 2
+    slots = slots_with_holes(rng, T, n_pg * P)
+    say(f"int8 random {seed}: H={H} T={T} P={P} h={h} rot={ROTS[rot]} mag={mag}")
+    assert_same(run_int8(env, k, v, slots, n_pg, P, h, rot),
+                oracle_int8(k, v, slots, n_pg, P, h, rot), f"int8 random {seed}")
+
+
 def test_int8_edge_values(env):
     rng = np.random.default_rng(2)
     T, H, D = 64, 2, 128
