@@ -410,6 +410,10 @@ def bench_attention(args):
     from int4_kv_cache_amd import sawkv as S
 
     wl = W.ATTN_WORKLOADS[args.workload]
+    if args.heads:
+        # one GPU's share under tensor parallelism over KV heads: the same
+        # contexts and queries per KV head, fewer KV heads
+        wl = dataclasses.replace(wl, H=args.heads, Hq=wl.Hq // wl.H * args.heads)
     h = args.h or wl.h
     rot = {"none": 0, "k": 1, "kv": 2}[args.rot] if args.rot else wl.rot_mode
     dev = torch.device("cuda:0")
@@ -461,6 +465,18 @@ def bench_attention(args):
     ratio = float(np.median(rot_ms) / np.median(naive_ms))
     ratio_ci = bootstrap_ratio_ci(rot_ms, naive_ms)
 
+    # cold caches: an untimed 1 GiB read before every timed call (the pool of
+    # a shard, or of a small batch, fits the 256 MB last-level cache between
+    # back-to-back calls)
+    flush = Flush(torch, dev)
+    cold = flush.cold({"naive": naive, "rot": call}, 15, stream)
+    del flush
+    cold_out = {"rot_us": pct(cold["rot"]), "naive_us": pct(cold["naive"]),
+                "rot_over_naive": round(float(np.median(cold["rot"]) / np.median(cold["naive"])), 4),
+                "GBps_rot_median": round(nbytes / (np.median(cold["rot"]) * 1e-3) / 1e9, 1),
+                "launches": 15,
+                "flush": "1 GiB device read before every timed call (not timed)"}
+
     # other query-head groupings on the same pool (fresh queries): 8 per KV
     # head (64 query heads, as Llama-2-70B) and 1 (multi-head attention)
     groupings = []
@@ -484,7 +500,7 @@ def bench_attention(args):
                           "rot_over_naive": round(float(np.median(gr) / np.median(gn)), 4)})
         del cg, ng, qg
 
-    traffic = measured_traffic(wl.name, ATTN_SRC)
+    traffic = measured_traffic(wl.name, ATTN_SRC) if not args.heads else None
     out = {
         "metric": ATTN_METRIC,
         "value": round(gbps, 2),
@@ -522,6 +538,8 @@ def bench_attention(args):
                      "rot_over_naive": round(ratio, 4), "rot_over_naive_ci95": ratio_ci,
                      "rounds": rounds, "steps_per_round": n_ab},
         "settle": settle,
+        "cold": cold_out,
+        "cache_resident": nbytes <= LLC_BYTES,
         "other_head_groupings": groupings,
         "workspace_bytes": int(call.workspace.numel()),
         "kernel_source_hash": kernel_source_hash(ATTN_SRC),
@@ -725,7 +743,7 @@ def main():
                              "concurrency"])
     ap.add_argument("--h", type=int, default=None)
     ap.add_argument("--heads", type=int, default=None,
-                    help="KV heads per GPU (e.g. 1 or 2: the TP-8 / TP-4 share of 8 heads)")
+                    help="KV heads per GPU (e.g. 1 or 2: the TP-8 / TP-4 share of 8 heads; 'attn' keeps the query heads per KV head)")
     ap.add_argument("--rot", default=None, choices=["none", "k", "kv"])
     ap.add_argument("--cpu-sample", type=int, default=131072)
     ap.add_argument("--no-cpu", action="store_true")
