@@ -694,6 +694,54 @@ __device__ __forceinline__ void compute_step(const StepRegs& r, const uint32_t (
   }
 }
 
+// The step loop of a piece, double-buffered: step t0's registers are in one
+// set while the loads of step t0 + step go to the other. The body holds two
+// steps, so the two sets alternate without a copy (copying registers whose
+// loads are in flight waits for those loads), its loads go out without a
+// condition (past the end of the range they get an empty buffer range and
+// touch no memory), and the loop has one exit. So every path into a step's
+// arithmetic has the same loads issued after that step's own, and the
+// compiler's wait before the arithmetic leaves the next step's loads in
+// flight; a conditional issue, or a break after each step, made it wait for
+// those too, which left no load of the wave in flight while it computed.
+// An odd last step is computed after the loop from the set the loop filled.
+template <typename Issue, typename Step>
+__device__ __forceinline__ void pipelined_steps(const int t_begin, const int t_end, const int step,
+                                                StepRegs& ra, StepRegs& rb, Issue&& issue,
+                                                Step&& compute) {
+  const int nsteps = t_end > t_begin ? (t_end - t_begin + step - 1) / step : 0;
+  int t0 = t_begin;
+  for (int i = 0; i < nsteps / 2; ++i) {
+    issue(rb, t0 + step);
+    compute(ra, t0);
+    issue(ra, t0 + 2 * step);
+    compute(rb, t0 + step);
+    t0 += 2 * step;
+  }
+  if (nsteps & 1) compute(ra, t0);
+  // the loads issued past the end are drained here (vmcnt 0, the other
+  // counters left alone): a later piece of the same wave then reuses their
+  // registers without the compiler holding its loop back for them
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// The plain form: one step of look-ahead issued only while steps remain, the
+// loaded set copied forward after each step. The copy waits for the next
+// step's loads, so the wave keeps no load in flight while it computes; the
+// other waves of the SIMD (three for most kernels here, whose registers the
+// pipelined form would push past 168) cover that latency instead, which
+// measured faster for the kernels other than eight queries per KV head.
+template <typename Issue, typename Step>
+__device__ __forceinline__ void lookahead_steps(const int t_begin, const int t_end, const int step,
+                                                StepRegs& cur, StepRegs& nxt, Issue&& issue,
+                                                Step&& compute) {
+  for (int t0 = t_begin; t0 < t_end; t0 += step) {
+    if (t0 + step < t_end) issue(nxt, t0 + step);
+    compute(cur, t0);
+    cur = nxt;
+  }
+}
+
 // Tokens [t_begin, t_end) of sequence b for KV head h, one wave: the
 // partial (reference exponent, denominator, weighted values) of the head's G
 // queries goes to partial row `part`. t_begin is a multiple of 16. WINDOWS:
@@ -743,33 +791,33 @@ __device__ __forceinline__ void head_piece(const ChunkParams& p, const int b, co
   // one step of look-ahead: the loads of step t0 + 32 are in flight while
   // step t0 is computed. EARLY: the first step's loads are issued before the
   // query is prepared, which then overlaps their latency.
-  StepRegs cur, nxt;
+  StepRegs ra, rb;
   u4_t bq[4];
   float cinit, F;
   if constexpr (EARLY) {
-    load_step<true, WINDOWS>(p, cur, t_begin, t_end, blk0, pages, h, ln, pages_next);
+    load_step<true, WINDOWS>(p, ra, t_begin, t_end, blk0, pages, h, ln, pages_next);
     prepare_query<G, false>(p.qp, qraw, lane, xs, bq, cinit, F);
   } else {
     prepare_query<G, false>(p.qp, qraw, lane, xs, bq, cinit, F);
-    load_step<false, WINDOWS>(p, cur, t_begin, t_end, blk0, pages, h, ln, pages_next);
+    load_step<false, WINDOWS>(p, ra, t_begin, t_end, blk0, pages, h, ln, pages_next);
   }
   const float F4 = 4.0f * F;
-  for (int t0 = t_begin; t0 < t_end; t0 += kStep) {
-    const int t1 = t0 + kStep;
-    if (t1 < t_end) {
-      if constexpr (WINDOWS) {
-        // the next step's first tile opens the next 64 pages (wave-uniform):
-        // their ids were loaded with the previous window's, the following
-        // ones go out now, 64 pages before a tile needs them
-        if (t1 / p.P - blk0 >= 64) {
-          blk0 += 64;
-          pages = pages_next;
-          pages_next = lane <= blk_last - blk0 - 64 ? bt_row[blk0 + 64 + lane] : -1;
-        }
+  auto issue = [&](StepRegs& r, const int t1) {
+    if constexpr (WINDOWS) {
+      // the step's first tile opens the next 64 pages (wave-uniform)
+      if (t1 < t_end && t1 / p.P - blk0 >= 64) {
+        // (their ids were loaded with the previous window's; the following
+        // ones go out now, lanes past the range's last page reading that
+        // page's id again: in bounds, and no tile reads those lanes)
+        blk0 += 64;
+        pages = pages_next;
+        pages_next = bt_row[min(blk0 + 64 + lane, blk_last)];
       }
-      load_step<false, WINDOWS>(p, nxt, t1, t_end, blk0, pages, h, ln, pages_next);
     }
-    sstage[lane] = (uint16_t)cur.sc;
+    load_step<false, WINDOWS>(p, r, t1, t_end, blk0, pages, h, ln, pages_next);
+  };
+  auto step = [&](const StepRegs& r, const int t0) {
+    sstage[lane] = (uint16_t)r.sc;
     __builtin_amdgcn_wave_barrier();
     uint32_t ks[2][2], vs[2][2];
 #pragma unroll
@@ -782,10 +830,10 @@ __device__ __forceinline__ void head_piece(const ChunkParams& p, const int b, co
       vs[T][1] = vv.y;
     }
     __builtin_amdgcn_wave_barrier();
-    const bool mask = !(cur.ok[0] && cur.ok[1] && t1 <= t_end);
-    compute_step<G>(cur, ks, vs, bq, cinit, F, F4, a, g, n, t0, t_end, mask);
-    cur = nxt;
-  }
+    const bool mask = !(r.ok[0] && r.ok[1] && t0 + kStep <= t_end);
+    compute_step<G>(r, ks, vs, bq, cinit, F, F4, a, g, n, t0, t_end, mask);
+  };
+  lookahead_steps(t_begin, t_end, kStep, ra, rb, issue, step);
 
   // ---- chunk partial ----
   float l = rows_sum(a.l);
@@ -1115,6 +1163,12 @@ __device__ __forceinline__ void pair_piece(const ChunkParams& p, const int b, co
   // faster with ordinary loads up to 64 sequences, because it then stays
   // cached between calls.
   constexpr int kAux = 2;
+  // eight queries per KV head pipeline the step loop (their steps carry the
+  // most arithmetic, which the pipelined form overlaps with the next step's
+  // loads: 64 query heads over 256 contexts of up to 8000 tokens 5 % faster,
+  // over 32 of 32768 9 %, although the registers leave two waves per SIMD);
+  // the other groupings measured 1-5 % slower pipelined
+  constexpr bool kPipe = GR == 8;
   int lane = threadIdx.x;
   // in the lean kernel's loop over ranges, the lane's load offsets are
   // derived anew for every piece instead of being held across the loop (the
@@ -1166,32 +1220,33 @@ __device__ __forceinline__ void pair_piece(const ChunkParams& p, const int b, co
 
   // EARLY: the first step's loads are issued before the query is prepared,
   // which then overlaps their latency
-  StepRegs cur, nxt;
+  StepRegs ra, rb;
   u4_t bq[4], bq_lo[4];
   float cinit, F;
   if constexpr (EARLY) {
-    load_pair_step<true, kAux>(p, cur, t_begin, t_end, blk0, pages, h0, ln);
+    load_pair_step<true, kAux>(p, ra, t_begin, t_end, blk0, pages, h0, ln);
     prepare_query<G, true>(p.qp, qraw, lane, xs, bq, cinit, F, bq_lo);
   } else {
     prepare_query<G, true>(p.qp, qraw, lane, xs, bq, cinit, F, bq_lo);
-    load_pair_step<false, kAux>(p, cur, t_begin, t_end, blk0, pages, h0, ln);
+    load_pair_step<false, kAux>(p, ra, t_begin, t_end, blk0, pages, h0, ln);
   }
   const float F4 = 4.0f * F;
-  for (int t0 = t_begin; t0 < t_end; t0 += 16) {
-    const int t1 = t0 + 16;
-    if (t1 < t_end) {
-      if constexpr (WINDOWS) {
-        // the next step opens the next 64 pages (wave-uniform): their ids
-        // were loaded with the previous window's, the following ones go out now
-        if (t1 / p.P - blk0 >= 64) {
-          blk0 += 64;
-          pages = pages_next;
-          pages_next = lane <= blk_last - blk0 - 64 ? bt_row[blk0 + 64 + lane] : -1;
-        }
+  auto issue = [&](StepRegs& r, const int t1) {
+    if constexpr (WINDOWS) {
+      // the step opens the next 64 pages (wave-uniform)
+      if (t1 < t_end && t1 / p.P - blk0 >= 64) {
+        // (their ids were loaded with the previous window's; the following
+        // ones go out now, lanes past the range's last page reading that
+        // page's id again: in bounds, and no tile reads those lanes)
+        blk0 += 64;
+        pages = pages_next;
+        pages_next = bt_row[min(blk0 + 64 + lane, blk_last)];
       }
-      load_pair_step<false, kAux>(p, nxt, t1, t_end, blk0, pages, h0, ln);
     }
-    sstage[lane] = (uint16_t)cur.sc;
+    load_pair_step<kPipe, kAux>(p, r, t1, t_end, blk0, pages, h0, ln);
+  };
+  auto step = [&](const StepRegs& r, const int t0) {
+    sstage[lane] = (uint16_t)r.sc;
     __builtin_amdgcn_wave_barrier();
     uint32_t ks[2][2], vs[2][2];
 #pragma unroll
@@ -1204,10 +1259,13 @@ __device__ __forceinline__ void pair_piece(const ChunkParams& p, const int b, co
       vs[T][1] = vv.y;
     }
     __builtin_amdgcn_wave_barrier();
-    const bool mask = !(cur.ok[0] && t1 <= t_end);
-    compute_pair_step<G>(cur, ks, vs, bq, bq_lo, cinit, F, F4, a, g, n, head_ok, t0, t_end, mask);
-    cur = nxt;
-  }
+    const bool mask = !(r.ok[0] && t0 + 16 <= t_end);
+    compute_pair_step<G>(r, ks, vs, bq, bq_lo, cinit, F, F4, a, g, n, head_ok, t0, t_end, mask);
+  };
+  if constexpr (kPipe)
+    pipelined_steps(t_begin, t_end, 16, ra, rb, issue, step);
+  else
+    lookahead_steps(t_begin, t_end, 16, ra, rb, issue, step);
 
   // ---- partial ----
   const float l = rows_sum(head_ok && (G == 8 || (n & 4) == 0) ? a.l : 0.0f);
@@ -1728,8 +1786,13 @@ Layout make_layout(int64_t B, int32_t Hq, int32_t H, int64_t max_context) {
   // per KV head run the single-head kernel on such grids, whose waves carry
   // twice the arithmetic of a head pair's per token and prefer longer chunks
   // (64 query heads, µs at 16 / 24 / 48 sequences: 29.8 / 40.2 / 64.2 with
-  // 4096 against 33.9 / 46.2 / 69.3 with 8192; 32 query heads lose with 4096)
-  const int64_t enough = Hq / H == 8 ? 4096 : 8192;
+  // 4096 against 33.9 / 46.2 / 69.3 with 8192; 32 query heads lose with 4096).
+  // An odd H runs the single-head kernel at every group size and prefers the
+  // longer chunks too (cold caches, contexts of up to 8000: 1 KV head x 128 /
+  // 256 / 448 sequences 30.5 / 44.0 / 70.6 µs against 33.6 / 48.1 / 79.0;
+  // 3 x 80: 47.8 against 57.4; 5 x 48: 44.0 against 54.3; one loss, 3 x 128:
+  // 63.3 against 60.6)
+  const int64_t enough = (Hq / H == 8 || H % 2 == 1) ? 4096 : 8192;
   while (C > 128 && B * H * ((max_context + C - 1) / C) < enough) C >>= 1;
   // a grid that cannot fill the chip even at 128 tokens (one or two long
   // sequences): halve once more, fewer serial steps per wave
