@@ -191,13 +191,13 @@ def widen_tables(x, max_context):
     return dict(x, block_tables=bt)
 
 
-# Eight queries per KV head over an even head count run the head-pair kernel
-# (16 queries per wave) once the grid, sequences x chunk slots x head pairs
-# with the chunk slots set by max_context, is deep enough. These cases keep
-# the short, masked attn_small contexts (0 to 1300 tokens, so the oracle stays
-# cheap) and pass a large max_context, which deepens the grid: 50000 gives
-# 256-token chunks, first loads before the query preparation; 2^17 512-token
-# chunks; 2^19 1024-token chunks, first loads after the query preparation.
+# Eight queries per KV head over an even head count, the short, masked
+# attn_small contexts (0 to 1300 tokens, so the oracle stays cheap) under a
+# large max_context: 50000 keeps the chunk form, where nine sequences give too
+# few blocks for the head-pair kernel, so the single-head kernel runs
+# (512-token chunks); 2^17 and 2^19 take the lean split, whose head-pair
+# kernel for eight queries runs the pipelined step loop over ranges that hold
+# several of these sequences each.
 @pytest.mark.parametrize("max_context,P,rot,h", [
     (50000, 16, O.ROT_KV, 128), (50000, 16, O.ROT_NONE, 128), (1 << 17, 16, O.ROT_K, 16),
     (1 << 17, 16, O.ROT_KV, 64), (1 << 17, 32, O.ROT_KV, 32), (1 << 17, 64, O.ROT_K, 128),
@@ -386,8 +386,9 @@ def test_lean_ranges_over_many_pages(env, Hq):
 # odd KV-head counts (a tensor-parallel shard's one or three heads): one wave per
 # (range, head), from 128 steps per wave if every context had max_context
 # tokens; 1024 sequences of 0-300 tokens under max_context 8192 leave most of
-# the 3072 (one head) or 1024 (three heads) waves per head with one step or none
-@pytest.mark.parametrize("Hq,H", [(4, 1), (8, 1), (12, 3)])
+# the 3072 (one head) or 1024 (three heads) waves per head with one step or none;
+# every group size of the single-head lean kernel (1, 2, 4 and 8 queries per head)
+@pytest.mark.parametrize("Hq,H", [(4, 1), (8, 1), (12, 3), (1, 1), (2, 1), (6, 3)])
 def test_lean_single_head(env, Hq, H):
     rng = np.random.default_rng(Hq + H)
     lens = np.where(rng.random(1024) < 0.15, 0, rng.integers(1, 301, size=1024))
@@ -460,6 +461,34 @@ def test_more_sequences_than_the_lean_split_takes(env):
     rng = np.random.default_rng(11)
     lens = rng.integers(0, 64, size=1025)
     lens_case(env, 32, lens, 768, wid=99)
+
+
+# More than 1024 sequences take the chunk form. Contexts of 0-700 tokens give
+# pieces of every step count up to 44, odd and even, exact multiples of 16 and
+# one token past them; max_context sets the grid: 768 with eight queries per
+# KV head is the head-pair kernel's pipelined step loop (two steps per pass,
+# loads past the end of a chunk issued with an empty range) in 512-token
+# chunks with the first loads before the query preparation; 3000 gives
+# 1024-token chunks (512 for three KV heads) and more than 12 288 blocks, so
+# the first loads follow the query preparation, for the pipelined head-pair
+# kernel, the plain one (four queries per head) and the single-head kernel
+# (three KV heads).
+@pytest.mark.parametrize("Hq,H,max_context,rot", [(64, 8, 768, O.ROT_K), (64, 8, 3000, O.ROT_KV),
+                                                  (32, 8, 3000, O.ROT_K), (12, 3, 3000, O.ROT_KV)])
+def test_chunk_form_more_than_1024_sequences(env, Hq, H, max_context, rot):
+    rng = np.random.default_rng(max_context + Hq)
+    lens = rng.integers(0, 701, size=1100)
+    lens[:44] = 16 * np.arange(44)
+    lens[44:88] = 16 * np.arange(44) + 1
+    wl = small(B=1100, Hq=Hq, H=H, ctx=("list", tuple(int(v) for v in lens)), rot_mode=rot,
+               wid=97 + Hq, masked=3)
+    x = widen_tables(W.attn_inputs(wl), max_context)
+    say(f"attn chunk form B=1100 Hq={Hq} H={H} max_context={max_context} rot={ROTS[rot]}")
+    got = run_gpu(env, x, max_context, 128, rot)
+    ref = run_oracle(x, 128, rot, max_context=max_context)
+    check(got, ref, tolerance(x, 128, rot, np.arange(1100), ref, max_context=max_context),
+          f"chunk form B=1100 Hq={Hq} H={H} max_context={max_context}")
+    assert not got[lens == 0].any()
 
 
 # --------------------------------------------------------------------------
