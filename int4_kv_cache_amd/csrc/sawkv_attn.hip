@@ -726,11 +726,14 @@ __device__ __forceinline__ void pipelined_steps(const int t_begin, const int t_e
 }
 
 // The plain form: one step of look-ahead issued only while steps remain, the
-// loaded set copied forward after each step. The copy waits for the next
-// step's loads, so the wave keeps no load in flight while it computes; the
-// other waves of the SIMD (three for most kernels here, whose registers the
-// pipelined form would push past 168) cover that latency instead, which
-// measured faster for the kernels other than eight queries per KV head.
+// loaded set copied forward after each step. The compiler's wait before a
+// step's arithmetic also covers the next step's loads (the last step's path,
+// which issues none, merges into it), so the wave keeps no load in flight
+// while it computes, and the other waves of the SIMD (three for these
+// kernels, whose registers the pipelined form would push past 168) cover the
+// latency instead. That measured faster than the pipelined form for every
+// grouping but eight queries per KV head, and faster than this loop with its
+// loads issued on every step (which leaves them in flight at three waves).
 template <typename Issue, typename Step>
 __device__ __forceinline__ void lookahead_steps(const int t_begin, const int t_end, const int step,
                                                 StepRegs& cur, StepRegs& nxt, Issue&& issue,
