@@ -1148,7 +1148,7 @@ __device__ __forceinline__ void compute_pair_step(const StepRegs& r, const uint3
 // slots per head for GR <= 4 (see load_query_pair), 8 for GR = 8; with GR = 1
 // or 2 the spare slots repeat a query: the extra arithmetic is hidden behind
 // the loads, and the wave still reads whole lines.
-template <int GR, bool EARLY, bool WINDOWS>
+template <int GR, bool EARLY, bool WINDOWS, bool PIPE>
 __device__ __forceinline__ void pair_piece(const ChunkParams& p, const int b, const int hp,
                                            const int t_begin, const int t_end,
                                            const int64_t part, uint16_t* sstage,
@@ -1166,12 +1166,8 @@ __device__ __forceinline__ void pair_piece(const ChunkParams& p, const int b, co
   // faster with ordinary loads up to 64 sequences, because it then stays
   // cached between calls.
   constexpr int kAux = 2;
-  // eight queries per KV head pipeline the step loop (their steps carry the
-  // most arithmetic, which the pipelined form overlaps with the next step's
-  // loads: 64 query heads over 256 contexts of up to 8000 tokens 5 % faster,
-  // over 32 of 32768 9 %, although the registers leave two waves per SIMD);
-  // the other groupings measured 1-5 % slower pipelined
-  constexpr bool kPipe = GR == 8;
+  // PIPE: the pipelined step loop (see pipelined_steps)
+  constexpr bool kPipe = PIPE;
   int lane = threadIdx.x;
   // in the lean kernel's loop over ranges, the lane's load offsets are
   // derived anew for every piece instead of being held across the loop (the
@@ -1338,7 +1334,7 @@ __device__ __forceinline__ void pair_piece(const ChunkParams& p, const int b, co
 
 // One (chunk, sequence, head pair) per block: chunk c covers tokens
 // [c C, (c + 1) C) of the sequence.
-template <int GR, bool EARLY>
+template <int GR, bool EARLY, bool PIPE>
 __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
   __shared__ uint16_t sstage[64];
   __shared__ float xs[2 * pair_slots<GR>()][kD];
@@ -1370,7 +1366,7 @@ __global__ __launch_bounds__(64) void attn_chunk_pair_kernel(ChunkParams p) {
   const int t_begin = c * p.C;
   if (t_begin >= L) return;
   const int t_end = min(t_begin + p.C, L);
-  pair_piece<GR, EARLY, false>(p, b, hp, t_begin, t_end, part, sstage, xs);
+  pair_piece<GR, EARLY, false, PIPE>(p, b, hp, t_begin, t_end, part, sstage, xs);
 }
 
 // Equal work per wave: the 16-token steps of all sequences, in sequence
@@ -1492,7 +1488,7 @@ __device__ __forceinline__ void lean_empty(const ChunkParams& p, int64_t row, in
   }
 }
 
-template <int GR>
+template <int GR, bool PIPE>
 __global__ __launch_bounds__(64) void attn_lean_pair_kernel(ChunkParams p) {
   __shared__ uint16_t sstage[64];
   __shared__ float xs[2 * pair_slots<GR>()][kD];
@@ -1511,7 +1507,7 @@ __global__ __launch_bounds__(64) void attn_lean_pair_kernel(ChunkParams p) {
     return;
   }
   lean_walk(p, b, s0, rem, [&](int bb, int t_begin, int t_end) {
-    pair_piece<GR, true, true>(p, bb, hp, t_begin, t_end, (int64_t)bb + k, sstage, xs);
+    pair_piece<GR, true, true, PIPE>(p, bb, hp, t_begin, t_end, (int64_t)bb + k, sstage, xs);
   });
 }
 
@@ -1863,9 +1859,27 @@ const void* const kChunk[2][4] = {
     {(void*)&attn_chunk_kernel<1, true>, (void*)&attn_chunk_kernel<2, true>,
      (void*)&attn_chunk_kernel<4, true>, (void*)&attn_chunk_kernel<8, true>}};
 // [G index][first-step order]
-#define SAWKV_PAIR(GR) \
-  {(void*)&attn_chunk_pair_kernel<GR, false>, (void*)&attn_chunk_pair_kernel<GR, true>}
-const void* const kChunkPair[4][2] = {SAWKV_PAIR(1), SAWKV_PAIR(2), SAWKV_PAIR(4), SAWKV_PAIR(8)};
+// The head-pair kernels come with the plain step loop and the pipelined one
+// (pipelined_steps), [G index][early][pipelined]. The pipelined loop keeps
+// the next step's loads in flight during a step's arithmetic at two waves per
+// SIMD instead of three. It pays where a step carries the most arithmetic
+// (eight queries per KV head: 64 query heads over 256 contexts of up to 8000
+// tokens 247 -> 236 us, over 32 of 32768 cold 229 -> 208 us) and where a
+// step's loads are contiguous (two KV heads, whose token rows are one pair's
+// 128-byte line: pages of 16 tokens read as 2 KB blocks; one pair over 256
+// contexts of up to 8000 tokens with 1, 2 or 4 queries per head 68-74 ->
+// 64-70 us back to back, 72-78 -> 69-72 us cold; over 64 contexts of 32768
+// 113 -> 107 us); with more heads each wave
+// reads one 128-byte line of every token row, and the third wave per SIMD
+// measured faster (32 query heads over 8 KV heads 1-3 % slower pipelined).
+// Eight queries per KV head have only the pipelined form.
+#define SAWKV_PAIR(GR, PLAIN)                                              \
+  {{(void*)&attn_chunk_pair_kernel<GR, false, PLAIN>,                     \
+    (void*)&attn_chunk_pair_kernel<GR, false, true>},                     \
+   {(void*)&attn_chunk_pair_kernel<GR, true, PLAIN>,                      \
+    (void*)&attn_chunk_pair_kernel<GR, true, true>}}
+const void* const kChunkPair[4][2][2] = {SAWKV_PAIR(1, false), SAWKV_PAIR(2, false),
+                                         SAWKV_PAIR(4, false), SAWKV_PAIR(8, true)};
 #undef SAWKV_PAIR
 
 // A grid of at most four rounds of resident chunk waves (3 per SIMD on 256
@@ -1887,12 +1901,14 @@ constexpr int64_t kPairEightBlocks = 2 * 3 * 4 * 256;
 using sawkv::attn::attn_lean_kernel;
 using sawkv::attn::attn_lean_pair_kernel;
 
-// [head pairs][G index]
-const void* const kLean[2][4] = {
+// [form: single head, head pairs, head pairs pipelined][G index]
+const void* const kLean[3][4] = {
     {(void*)&attn_lean_kernel<1>, (void*)&attn_lean_kernel<2>, (void*)&attn_lean_kernel<4>,
      (void*)&attn_lean_kernel<8>},
-    {(void*)&attn_lean_pair_kernel<1>, (void*)&attn_lean_pair_kernel<2>,
-     (void*)&attn_lean_pair_kernel<4>, (void*)&attn_lean_pair_kernel<8>}};
+    {(void*)&attn_lean_pair_kernel<1, false>, (void*)&attn_lean_pair_kernel<2, false>,
+     (void*)&attn_lean_pair_kernel<4, false>, (void*)&attn_lean_pair_kernel<8, true>},
+    {(void*)&attn_lean_pair_kernel<1, true>, (void*)&attn_lean_pair_kernel<2, true>,
+     (void*)&attn_lean_pair_kernel<4, true>, (void*)&attn_lean_pair_kernel<8, true>}};
 
 // Lean waves per head group on the device of `stream`: the waves the device
 // keeps resident at once (occupancy of the lean kernel times compute units,
@@ -1900,9 +1916,9 @@ const void* const kLean[2][4] = {
 // and max_per_group per group, a multiple of 8; 0 if the device cannot say.
 constexpr int kLeanDevices = 64;
 std::mutex g_lean_mu;
-int g_lean_resident[kLeanDevices][2][4] = {};
+int g_lean_resident[kLeanDevices][3][4] = {};
 
-int lean_waves_per_group(hipStream_t stream, int pair, int gi, int groups, int max_per_group) {
+int lean_waves_per_group(hipStream_t stream, int form, int gi, int groups, int max_per_group) {
   int dev = -1;
   if ((stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev)) != hipSuccess || dev < 0 ||
       dev >= kLeanDevices)
@@ -1910,14 +1926,14 @@ int lean_waves_per_group(hipStream_t stream, int pair, int gi, int groups, int m
   int resident;
   {
     std::lock_guard<std::mutex> lock(g_lean_mu);
-    resident = g_lean_resident[dev][pair][gi];
+    resident = g_lean_resident[dev][form][gi];
     if (resident == 0) {
       int per_cu = 0, cus = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kLean[pair][gi], 64, 0) != hipSuccess ||
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kLean[form][gi], 64, 0) != hipSuccess ||
           hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         per_cu = cus = 0;
       resident = per_cu > 0 && cus > 0 ? per_cu * cus : -1;
-      g_lean_resident[dev][pair][gi] = resident;
+      g_lean_resident[dev][form][gi] = resident;
     }
   }
   if (resident <= 0) return 0;
@@ -2027,9 +2043,13 @@ int attention_impl(const void* q, int64_t q_stride, const void* k_codes, const v
   mp.C = lay.C;
   mp.max_context = (int32_t)max_context;
 
+  // two KV heads: the pipelined step loop for every grouping (kChunkPair)
+  const int pipe = H == 2 ? 1 : 0;
+
   // the lean form: split plan, equal-steps waves, merge
   const int lean_pair = H % 2 == 0 ? 1 : 0;
-  const int nwp = lay.lean ? lean_waves_per_group(s, lean_pair, g_index(G), head_groups(H),
+  const int lean_form = lean_pair + pipe;
+  const int nwp = lay.lean ? lean_waves_per_group(s, lean_form, g_index(G), head_groups(H),
                                                    lay.lean_waves)
                            : 0;
   if (nwp >= 8 && (lean_pair || B * ((max_context + 15) / 16) >= kLeanMinHeadSteps * nwp)) {
@@ -2038,7 +2058,7 @@ int attention_impl(const void* q, int64_t q_stride, const void* k_codes, const v
     cp.lean_waves = nwp;
     cp.lean_seqs = (int32_t)B;
     cp.lean_seq = reinterpret_cast<int2*>(ws + lay.l_seq);
-    if ((st = launch64(kLean[lean_pair][g_index(G)], (int64_t)nwp * head_groups(H), &cp, s)))
+    if ((st = launch64(kLean[lean_form][g_index(G)], (int64_t)nwp * head_groups(H), &cp, s)))
       return st;
     mp.part_o = cp.part_o;
     mp.part_ml = cp.part_ml;
@@ -2055,7 +2075,7 @@ int attention_impl(const void* q, int64_t q_stride, const void* k_codes, const v
   const int64_t chunk_blocks = ((B * lay.NC + 7) / 8) * 8 * groups;
   const int early = chunk_blocks <= kEarlyIssueBlocks ? 1 : 0;
   if (max_context > 0 &&
-      (st = launch64(pair ? kChunkPair[g_index(G)][early]
+      (st = launch64(pair ? kChunkPair[g_index(G)][early][pipe]
                           : kChunk[early][g_index(G)],
                      chunk_blocks, &cp, s)))
     return st;
