@@ -1865,14 +1865,16 @@ const void* const kChunk[2][4] = {
 // SIMD instead of three. It pays where a step carries the most arithmetic
 // (eight queries per KV head: 64 query heads over 256 contexts of up to 8000
 // tokens 247 -> 236 us, over 32 of 32768 cold 229 -> 208 us) and where a
-// step's loads are contiguous (two KV heads, whose token rows are one pair's
-// 128-byte line: pages of 16 tokens read as 2 KB blocks; one pair over 256
-// contexts of up to 8000 tokens with 1, 2 or 4 queries per head 68-74 ->
-// 64-70 us back to back, 72-78 -> 69-72 us cold; over 64 contexts of 32768
-// 113 -> 107 us); with more heads each wave
-// reads one 128-byte line of every token row, and the third wave per SIMD
-// measured faster (32 query heads over 8 KV heads 1-3 % slower pipelined).
-// Eight queries per KV head have only the pipelined form.
+// wave's loads cover much of each token row. With two KV heads a row is the
+// pair's 128-byte line, so a 16-token page reads as one 2 KB block (one pair
+// over 256 contexts of up to 8000 tokens, 1, 2 or 4 queries per head: 68-74
+// -> 64-70 us back to back, 72-78 -> 69-72 us cold; over 64 contexts of
+// 32768 113 -> 107 us); with four the pair's line is half of each row (lean
+// split, 256 contexts 116-121 -> 109-116 us, 128 contexts 69-72 -> 65 us; the
+// chunk form's grids 3 % slower, so they keep the plain loop); with eight a
+// wave reads a quarter of every row, and the third wave per SIMD measured
+// faster (32 query heads 1-3 % slower pipelined). Eight queries per KV head
+// have only the pipelined form.
 #define SAWKV_PAIR(GR, PLAIN)                                              \
   {{(void*)&attn_chunk_pair_kernel<GR, false, PLAIN>,                     \
     (void*)&attn_chunk_pair_kernel<GR, false, true>},                     \
@@ -2043,12 +2045,15 @@ int attention_impl(const void* q, int64_t q_stride, const void* k_codes, const v
   mp.C = lay.C;
   mp.max_context = (int32_t)max_context;
 
-  // two KV heads: the pipelined step loop for every grouping (kChunkPair)
+  // the pipelined step loop for every grouping (kChunkPair): two KV heads in
+  // either form, four in the lean split (the chunk form's grids there measured
+  // 3 % slower pipelined)
   const int pipe = H == 2 ? 1 : 0;
+  const int lean_pipe = H == 2 || H == 4 ? 1 : 0;
 
   // the lean form: split plan, equal-steps waves, merge
   const int lean_pair = H % 2 == 0 ? 1 : 0;
-  const int lean_form = lean_pair + pipe;
+  const int lean_form = lean_pair + lean_pipe;
   const int nwp = lay.lean ? lean_waves_per_group(s, lean_form, g_index(G), head_groups(H),
                                                    lay.lean_waves)
                            : 0;

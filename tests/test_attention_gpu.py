@@ -383,40 +383,40 @@ def test_lean_ranges_over_many_pages(env, Hq):
     lens_case(env, Hq, lens, 32768, seqs=seqs, wid=96 + Hq, masked=0)
 
 
-# Two KV heads (one GPU's share of an eight-head model at tensor parallelism
-# 4): each token row is the one head pair's 128-byte line, and the pair's lean
-# kernels run the pipelined step loop for every grouping. 1024 short
-# sequences under max_context 768 (about five steps per wave: pieces of one
-# step and up, odd and even counts, ranges crossing several sequences), then
-# 96 contexts of 24 000-32 768 tokens (ranges of about 90 steps, over more
-# than 64 pages, so the page ids change windows mid-range).
-@pytest.mark.parametrize("Hq", [2, 4, 8, 16])
-def test_lean_two_kv_heads_short(env, Hq):
-    rng = np.random.default_rng(Hq + 7)
+# Two or four KV heads (one GPU's share of an eight-head model at tensor
+# parallelism 4 or 2): the head pairs' lean kernels run the pipelined step
+# loop for every grouping. 1024 short sequences under max_context 768 (a few
+# steps per wave: pieces of one step and up, odd and even counts, ranges
+# crossing several sequences), then 96 contexts of 24 000-32 768 tokens over
+# two heads and 64 over four (ranges of about 90 and 120 steps, over more than
+# 64 pages, so the page ids change windows mid-range).
+@pytest.mark.parametrize("Hq,H", [(2, 2), (4, 2), (8, 2), (16, 2), (4, 4), (16, 4)])
+def test_lean_few_kv_heads_short(env, Hq, H):
+    rng = np.random.default_rng(Hq + 7 * H)
     lens = np.where(rng.random(1024) < 0.15, 0, rng.integers(1, 301, size=1024))
-    wl = small(B=1024, Hq=Hq, H=2, ctx=("list", tuple(int(v) for v in lens)),
-               rot_mode=O.ROT_KV, wid=120 + Hq)
+    wl = small(B=1024, Hq=Hq, H=H, ctx=("list", tuple(int(v) for v in lens)),
+               rot_mode=O.ROT_KV, wid=120 + Hq + H)
     x = widen_tables(W.attn_inputs(wl), 768)
-    say(f"attn lean two KV heads B=1024 Hq={Hq}")
+    say(f"attn lean B=1024 Hq={Hq} H={H}")
     got = run_gpu(env, x, 768, 128, O.ROT_KV)
     ref = run_oracle(x, 128, O.ROT_KV, max_context=768)
     check(got, ref, tolerance(x, 128, O.ROT_KV, np.arange(1024), ref, max_context=768),
-          f"lean two KV heads Hq={Hq}")
+          f"lean Hq={Hq} H={H}")
     assert not got[lens == 0].any()
 
 
-@pytest.mark.parametrize("Hq", [4, 8])
-def test_lean_two_kv_heads_long(env, Hq):
-    rng = np.random.default_rng(Hq + 9)
-    lens = rng.integers(24000, 32769, size=96)
-    wl = small(B=96, Hq=Hq, H=2, ctx=("list", tuple(int(v) for v in lens)), rot_mode=O.ROT_K,
-               wid=130 + Hq, masked=0)
+@pytest.mark.parametrize("Hq,H,B", [(4, 2, 96), (8, 2, 96), (16, 4, 64)])
+def test_lean_few_kv_heads_long(env, Hq, H, B):
+    rng = np.random.default_rng(Hq + 9 * H)
+    lens = rng.integers(24000, 32769, size=B)
+    wl = small(B=B, Hq=Hq, H=H, ctx=("list", tuple(int(v) for v in lens)), rot_mode=O.ROT_K,
+               wid=130 + Hq + H, masked=0)
     x = widen_tables(W.attn_inputs(wl), 32768)
-    say(f"attn lean two KV heads B=96 Hq={Hq} long contexts")
+    say(f"attn lean B={B} Hq={Hq} H={H} long contexts")
     got = run_gpu(env, x, 32768, 128, O.ROT_K)
-    seqs = np.unique(np.r_[np.argmin(lens), np.argmax(lens), rng.choice(96, 2, replace=False)])
+    seqs = np.unique(np.r_[np.argmin(lens), np.argmax(lens), rng.choice(B, 2, replace=False)])
     ref = run_oracle(x, 128, O.ROT_K, seqs=seqs)
-    check(got[seqs], ref, tolerance(x, 128, O.ROT_K, seqs, ref), f"lean two KV heads long Hq={Hq}")
+    check(got[seqs], ref, tolerance(x, 128, O.ROT_K, seqs, ref), f"lean long Hq={Hq} H={H}")
 
 
 # odd KV-head counts (a tensor-parallel shard's one or three heads): one wave per
